@@ -1,0 +1,60 @@
+"""The seeded generators: deterministic, topological trees, documented shapes."""
+import numpy as np
+import pytest
+
+import gdn_inputs as G
+
+
+def test_seeded_and_reproducible():
+    cfg = G.shrink(G.CONFIGS["bestfirst128"], N=40, H_v=4, H_k=2)
+    a = G.make_inputs(cfg, seed=0)
+    b = G.make_inputs(cfg, seed=0)
+    c = G.make_inputs(cfg, seed=1)
+    for key in ("parent", "q", "k", "v", "g", "beta", "S0"):
+        assert np.array_equal(a[key], b[key])
+    assert not np.array_equal(a["S0"], c["S0"])
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "chain64", "bestfirst128", "batched_commit"])
+def test_shapes_and_ranges(name):
+    cfg = G.CONFIGS[name]
+    x = G.make_inputs(cfg)
+    B, N, Hk, Hv, dk, dv = cfg.B, cfg.N, cfg.H_k, cfg.H_v, cfg.d_k, cfg.d_v
+    assert x["parent"].shape == (B, N) and x["parent"].dtype == np.int32
+    assert x["q"].shape == (B, N, Hk, dk) and x["k"].shape == (B, N, Hk, dk)
+    assert x["v"].shape == (B, N, Hv, dv)
+    assert x["g"].shape == (B, N, Hv) and (x["g"] <= 0).all()
+    assert ((x["beta"] > 0) & (x["beta"] < 1)).all()
+    assert x["S0"].shape == (B, Hv, dv, dk)
+    par = x["parent"]
+    idx = np.arange(N)
+    assert (par[:, 0] == -1).all() and (par >= -1).all() and (par < idx).all()
+    if cfg.dtype == "bf16":
+        for n in ("q", "k", "v"):
+            assert np.array_equal(G.bf16_bits_to_f32(x[n + "_bits"]), x[n])
+        nrm = np.linalg.norm(x["q"].astype(np.float64), axis=-1)
+        assert np.allclose(nrm, 1.0, atol=1e-2)
+    if cfg.commit:
+        assert ((x["accepted"] >= 0) & (x["accepted"] < N)).all()
+    if cfg.tree == "best_first":
+        st = G.tree_stats(par)
+        assert st["max_depth"] <= cfg.max_depth
+    if cfg.tree == "chain":
+        assert np.array_equal(par[0], idx - 1)
+
+
+def test_best_first_branching_and_depth_cap():
+    rng = G.rng_for(5)
+    par = G.tree_best_first(rng, 8, 256, 24)
+    st = G.tree_stats(par)
+    assert st["max_depth"] <= 24
+    counts = np.bincount(par[par >= 0].ravel())
+    assert counts.max() <= 8 * 4  # a node re-expanded after the heap runs dry may exceed 8
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(3).standard_normal(100000).astype(np.float32) * 7
+    x[:4] = [1.00390625, 1.01171875, -2.5e-40, 3.0e38]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(G.round_bf16_bits(x), want)
