@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark: GDN rollback-free tree verification on one MI355X.
+
+One step = one pass of the whole hot path over one batch: gdn_tree_verify
+(every node's output in one pass, S0 untouched) followed by gdn_commit_path
+(the accepted node's state), on the workload
+
+    best-first proposal trees, depth <= 16, B=32 sequences x N=128 nodes,
+    32 value heads sharing 16 key heads, d_k = d_v = 128,
+    bf16 q/k/v, fp32 g/beta/S0, fp32 outputs (synthetic, seeded).
+
+Inputs live in HBM before timing starts; R rotating input sets (>= 3x the
+256 MB Infinity Cache in total) keep the cache from serving the reads.
+
+Prints ONE JSON line.  `value` is nodes*heads per second of the whole step;
+the verify-only rate, the roofline of the dominant kernel (verify, measured
+with HIP events on the stream it runs on) and the fp64 CPU oracle timed on
+this host are reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN tree-verify nodes·heads/s per layer at B=32,N=128; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "bestfirst_b32n128"
+KERNEL_SOURCES = ["gdn_tree_api.cpp", "gdn_simple.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_verify_bestfirst_b32n128.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_deltanet_tree_gdn_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def verify_bytes(cfg) -> int:
+    """Algorithmic bytes of one verify: read q, k, v, g, beta, parent, S0
+    once, write o once (fp32)."""
+    B, N, Hk, Hv, dk, dv = cfg.B, cfg.N, cfg.H_k, cfg.H_v, cfg.d_k, cfg.d_v
+    e = 2 if cfg.dtype == "bf16" else 4
+    return (B * Hv * dv * dk * 4 + B * N * Hv * dv * 4 + B * N * Hv * dv * e
+            + 2 * B * N * Hk * dk * e + 2 * B * N * Hv * 4 + B * N * 4)
+
+
+def commit_bytes(cfg, path_len) -> int:
+    """Algorithmic bytes of one commit: read S0 and the accepted path's rows
+    (k per key head, v/g/beta per value head), parent and accepted; write
+    S_new."""
+    B, N, Hk, Hv, dk, dv = cfg.B, cfg.N, cfg.H_k, cfg.H_v, cfg.d_k, cfg.d_v
+    e = 2 if cfg.dtype == "bf16" else 4
+    rows = int(sum(path_len))
+    return (2 * B * Hv * dv * dk * 4 + rows * (Hk * dk * e + Hv * (dv * e + 8)) + B * N * 4 + B * 4)
+
+
+def read_traffic(per_launch_bytes):
+    """HBM traffic of one verify launch from committed rocprofv3 counters,
+    if they were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(sets0, cfg, max_seqs):
+    """The fp64 oracle (memoised form, as it stands) on a bounded sample of
+    the same inputs: the first `max_seqs` sequences of input set 0."""
+    import numpy as np
+    import oracle
+
+    nb = min(max_seqs, cfg.B)
+    host = {n: sets0[n][:nb].float().cpu().numpy().astype(np.float64) for n in ("q", "k", "v", "g", "beta", "S0")}
+    host["parent"] = sets0["parent"][:nb].cpu().numpy()
+    threads = min(os.cpu_count() or 1, 16)
+    t0 = time.perf_counter()
+    oracle.verify_inputs(host, memo=True, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": nb * cfg.N * cfg.H_v / dt, "unit": "nodes·heads/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 memoised oracle, verify of sequences 0..{nb - 1} of input set 0 "
+                      f"({nb}x{cfg.N} nodes x {cfg.H_v} heads), {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="only run verify back-to-back (for profiler runs); prints progress, no JSON")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 "
+              "(sharding is described in DESIGN.md, not run)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_deltanet_tree_gdn_amd as gdn
+    import gdn_inputs as G
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = G.CONFIGS[WORKLOAD]
+    gdn.load_library()
+
+    sets = []
+    for r in range(args.sets):
+        parent = G.make_tree(cfg, G.rng_for(args.seed, 1000 + r))
+        d = G.make_inputs_device(cfg, seed=args.seed, layer=r, parent=parent, device=dev)
+        d["accepted"] = torch.from_numpy(G.rng_for(args.seed, 2000 + r).integers(0, cfg.N, size=cfg.B)
+                                         .astype(np.int32)).to(dev)
+        d["o"] = torch.empty((cfg.B, cfg.N, cfg.H_v, cfg.d_v), dtype=torch.float32, device=dev)
+        d["S_new"] = torch.empty_like(d["S0"])
+        d["ctx"] = gdn.GdnContext.for_tensors(d["q"], d["v"], d["parent"])
+        sets.append(d)
+    anc_depth = [G.tree_stats(s["parent"].cpu().numpy()) for s in sets]
+    # path length of each accepted node (for the commit's algorithmic bytes)
+    path_lens = []
+    for s in sets:
+        par = s["parent"].cpu().numpy()
+        acc = s["accepted"].cpu().numpy()
+        lens = []
+        for b in range(cfg.B):
+            n, x = 0, int(acc[b])
+            while x >= 0:
+                n += 1
+                x = int(par[b, x])
+            lens.append(n)
+        path_lens.append(lens)
+
+    stream = torch.cuda.current_stream()
+
+    def verify(s):
+        gdn.gdn_tree_verify(s["ctx"], s["q"], s["k"], s["v"], s["g"], s["beta"], s["parent"], s["S0"],
+                            o=s["o"], stream=stream)
+
+    def commit(s):
+        gdn.gdn_commit_path(s["ctx"], s["accepted"], S_new=s["S_new"], stream=stream)
+
+    if args.kernel_only:
+        for i in range(args.warmup + args.steps):
+            verify(sets[i % len(sets)])
+            if i % 50 == 0:
+                torch.cuda.synchronize()
+                print(f"kernel-only: {i} verify calls", flush=True)
+        torch.cuda.synchronize()
+        print("kernel-only: done", flush=True)
+        return
+
+    for i in range(args.warmup):
+        s = sets[i % len(sets)]
+        verify(s)
+        commit(s)
+    torch.cuda.synchronize()
+    for s in sets:
+        gdn.gdn_ctx_status(s["ctx"])
+
+    # --- the timed region: K whole steps --------------------------------------
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        s = sets[i % len(sets)]
+        verify(s)
+        commit(s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # --- per-kernel averages (HIP events on the launch stream) ---------------
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            fn(sets[i % len(sets)])
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    verify_ms = timed(verify, args.steps)
+    commit_ms = timed(commit, args.steps)
+    for s in sets:
+        gdn.gdn_ctx_status(s["ctx"])
+
+    nh = cfg.B * cfg.N * cfg.H_v
+    vbytes = verify_bytes(cfg)
+    cbytes = float(np.mean([commit_bytes(cfg, pl) for pl in path_lens]))
+    achieved = vbytes / (verify_ms * 1e-3) / 1e9
+    traffic = read_traffic(vbytes)
+    out = {
+        "metric": METRIC,
+        "value": nh / (step_ms * 1e-3),
+        "unit": "nodes·heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded best-first trees and N(0,1)-derived tensors; no model weights)",
+        "config": {"workload": WORKLOAD, "B": cfg.B, "N": cfg.N, "H_k": cfg.H_k, "H_v": cfg.H_v,
+                   "d_k": cfg.d_k, "d_v": cfg.d_v, "qkv": cfg.dtype, "state": "f32", "output": "f32",
+                   "tree": f"best_first depth<={cfg.max_depth}",
+                   "mean_strict_ancestors": float(np.mean([a["mean_strict_ancestors"] for a in anc_depth])),
+                   "max_depth": int(max(a["max_depth"] for a in anc_depth)),
+                   "rotating_sets": len(sets), "step": "gdn_tree_verify + gdn_commit_path"},
+        "verify": {"ms": verify_ms, "nodes_heads_per_s": nh / (verify_ms * 1e-3),
+                   "algorithmic_bytes": vbytes, "GBps": achieved},
+        "commit": {"ms": commit_ms, "algorithmic_bytes": cbytes, "GBps": cbytes / (commit_ms * 1e-3) / 1e9},
+        "roofline": {"bound": "hbm", "kernel": "gdn_tree_verify", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic},
+        "wall_s_timed_region": wall,
+    }
+    if args.cpu_seqs > 0:
+        out["cpu_baseline"] = cpu_baseline(sets[0], cfg, args.cpu_seqs)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,52 @@
+// gdn_internal.h -- host-side launch interface shared by the C-ABI layer and
+// the kernel translation units of the GDN tree-verification library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "gdn_tree.h"
+
+namespace gdn {
+
+constexpr int kMaxN = 256;  // largest tree the kernels accept
+
+// Arguments of one tree verification (all device pointers, layouts as in
+// gdn_tree.h).
+struct VerifyArgs {
+    int B, N, H_k, H_v, d_k, d_v;
+    int qkv_dtype;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const int32_t* parent;
+    const float* S0;
+    float* o;
+    int32_t* tree_status;  // [B]: 0 or GDN_ERR_TREE
+};
+
+// Arguments of one accepted-path commit.
+struct CommitArgs {
+    int B, N, H_k, H_v, d_k, d_v;
+    int qkv_dtype;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const int32_t* parent;
+    const float* S0;
+    const int32_t* accepted;
+    float* S_new;
+    int32_t* accept_status;  // [B]: 0 or GDN_ERR_ACCEPT
+};
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
+hipError_t launch_ancestors(int B, int N, const int32_t* parent, uint32_t* anc, int32_t* depth,
+                            int32_t* tree_status, hipStream_t stream);
+
+}  // namespace gdn

@@ -41,7 +41,8 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "rng_for", "tree_uniform", "tree_chain", "tree_best_first",
-    "round_bf16_bits", "bf16_bits_to_f32", "make_inputs", "tree_stats",
+    "round_bf16_bits", "bf16_bits_to_f32", "make_inputs", "make_inputs_device", "tree_stats",
+    "to_device", "shrink",
 ]
 
 
@@ -255,3 +256,57 @@ def make_inputs(cfg: Config, seed: int = 0, layer: int = 0, parent: Optional[np.
 def shrink(cfg: Config, **kw) -> Config:
     """A copy of ``cfg`` with some fields replaced (smaller test sizes)."""
     return dataclasses.replace(cfg, **kw)
+
+
+def make_inputs_device(cfg: Config, seed: int = 0, layer: int = 0, parent: Optional[np.ndarray] = None,
+                       device="cuda"):
+    """The same recipe drawn on the device with torch's generator (for the
+    48-layer stress workload, where host generation would dominate).
+
+    Values follow the distributions of :func:`make_inputs` but not its exact
+    numbers.  Returns torch tensors: q, k, v (bf16 or fp32), g, beta, S0
+    (fp32), parent (int32; the given shared tree, else one drawn with numpy).
+    """
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed((int(seed) * 1_000_003 + int(layer)) & 0x7FFFFFFFFFFFFFFF)
+    B, N, Hk, Hv, dk, dv = cfg.B, cfg.N, cfg.H_k, cfg.H_v, cfg.d_k, cfg.d_v
+    if parent is None:
+        parent = make_tree(cfg, rng_for(seed, layer))
+    par = torch.from_numpy(np.ascontiguousarray(parent, dtype=np.int32)).to(device)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+    q = randn(B, N, Hk, dk)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = randn(B, N, Hk, dk)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = randn(B, N, Hv, dv)
+    g = -torch.nn.functional.softplus(randn(B, N, Hv))
+    beta = torch.sigmoid(randn(B, N, Hv))
+    S0 = 0.02 * randn(B, Hv, dv, dk)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    return {"parent": par, "q": q.to(dt).contiguous(), "k": k.to(dt).contiguous(), "v": v.to(dt).contiguous(),
+            "g": g.contiguous(), "beta": beta.contiguous(), "S0": S0.contiguous(), "cfg": cfg}
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """Host arrays from :func:`make_inputs` as torch tensors on ``device``
+    (bf16 tensors are rebuilt from the exact bit patterns)."""
+    import torch
+
+    out = {}
+    for name in ("q", "k", "v"):
+        if name + "_bits" in inp:
+            t = torch.from_numpy(inp[name + "_bits"].view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(inp[name], dtype=np.float32))
+        out[name] = t.to(device).contiguous()
+    for name in ("g", "beta", "S0"):
+        out[name] = torch.from_numpy(np.ascontiguousarray(inp[name], dtype=np.float32)).to(device)
+    out["parent"] = torch.from_numpy(np.ascontiguousarray(inp["parent"], dtype=np.int32)).to(device)
+    if "accepted" in inp:
+        out["accepted"] = torch.from_numpy(np.ascontiguousarray(inp["accepted"], dtype=np.int32)).to(device)
+    return out

@@ -1,0 +1,144 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_tree_gdn_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_tree.h")
+
+FAKE = 0x10000  # never dereferenced: every call below fails before touching it
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn_tree.so is not built: run __graft_entry__.build()")
+    return gdn.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(gdn.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def dims(**kw):
+    d = dict(B=2, N=16, H_k=2, H_v=4, d_k=128, d_v=128, qkv_dtype=gdn.GDN_BF16)
+    d.update(kw)
+    return gdn.Dims(**d)
+
+
+def make_ctx(lib, d):
+    h = ctypes.c_void_p()
+    n = lib.gdn_tree_workspace_bytes(ctypes.byref(d))
+    rc = lib.gdn_ctx_create(ctypes.byref(d), FAKE, n, ctypes.byref(h))
+    return rc, h
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(gdn.STATUS):
+        assert lib.gdn_status_string(code).decode() == name
+
+
+def test_workspace_bytes(lib):
+    n = lib.gdn_tree_workspace_bytes(ctypes.byref(dims(B=1000)))
+    assert n >= 8000 and n % 256 == 0
+    assert lib.gdn_tree_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=257), "GDN_ERR_SHAPE"), (dict(N=-1), "GDN_ERR_SHAPE"), (dict(B=-3), "GDN_ERR_SHAPE"),
+    (dict(H_v=3), "GDN_ERR_SHAPE"), (dict(H_k=0), "GDN_ERR_SHAPE"), (dict(d_k=96), "GDN_ERR_SHAPE"),
+    (dict(d_v=256), "GDN_ERR_SHAPE"), (dict(qkv_dtype=7), "GDN_ERR_DTYPE"),
+])
+def test_bad_dims_rejected(lib, kw, code):
+    rc, h = make_ctx(lib, dims(**kw))
+    assert gdn.STATUS[rc] == code
+    assert lib.gdn_last_error().decode()
+    assert not h.value
+
+
+def test_workspace_checks(lib):
+    d = dims()
+    h = ctypes.c_void_p()
+    assert gdn.STATUS[lib.gdn_ctx_create(ctypes.byref(d), None, 4096, ctypes.byref(h))] == "GDN_ERR_WORKSPACE"
+    assert gdn.STATUS[lib.gdn_ctx_create(ctypes.byref(d), FAKE, 4, ctypes.byref(h))] == "GDN_ERR_WORKSPACE"
+    assert gdn.STATUS[lib.gdn_ctx_create(ctypes.byref(d), FAKE + 16, 4096, ctypes.byref(h))] == "GDN_ERR_ALIGN"
+    assert gdn.STATUS[lib.gdn_ctx_create(ctypes.byref(d), FAKE, 4096, None)] == "GDN_ERR_NULL"
+
+
+def verify_args(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, parent=FAKE, S0=FAKE, o=FAKE)
+    a.update(over)
+    return [a[n] for n in ("q", "k", "v", "g", "beta", "parent", "S0", "o")]
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "parent", "S0", "o"])
+def test_verify_null_and_misaligned(lib, name):
+    rc, h = make_ctx(lib, dims())
+    assert rc == 0
+    try:
+        rc = lib.gdn_tree_verify(h, *verify_args(**{name: None}), None)
+        assert gdn.STATUS[rc] == "GDN_ERR_NULL"
+        assert name in lib.gdn_last_error().decode()
+        rc = lib.gdn_tree_verify(h, *verify_args(**{name: FAKE + 4}), None)
+        assert gdn.STATUS[rc] == "GDN_ERR_ALIGN"
+    finally:
+        lib.gdn_ctx_destroy(h)
+
+
+def test_commit_without_verify(lib):
+    rc, h = make_ctx(lib, dims())
+    assert rc == 0
+    try:
+        assert gdn.STATUS[lib.gdn_commit_path(h, FAKE, FAKE, None)] == "GDN_ERR_STATE"
+        # a verify that failed its checks does not arm the commit either
+        lib.gdn_tree_verify(h, *verify_args(q=None), None)
+        assert gdn.STATUS[lib.gdn_commit_path(h, FAKE, FAKE, None)] == "GDN_ERR_STATE"
+    finally:
+        lib.gdn_ctx_destroy(h)
+
+
+def test_empty_batch_is_noop(lib):
+    for d in (dims(B=0), dims(N=0)):
+        rc, h = make_ctx(lib, d)
+        assert rc == 0
+        try:
+            assert lib.gdn_tree_verify(h, *verify_args(q=None, o=None), None) == 0
+        finally:
+            lib.gdn_ctx_destroy(h)
+
+
+def test_null_ctx(lib):
+    assert gdn.STATUS[lib.gdn_tree_verify(None, *verify_args(), None)] == "GDN_ERR_NULL"
+    assert gdn.STATUS[lib.gdn_commit_path(None, FAKE, FAKE, None)] == "GDN_ERR_NULL"
+    assert gdn.STATUS[lib.gdn_ctx_status(None, None)] == "GDN_ERR_NULL"
+    assert lib.gdn_ctx_destroy(None) == 0
+
+
+def test_ancestors_arg_checks(lib):
+    d = dims(N=300)
+    assert gdn.STATUS[lib.gdn_tree_ancestors(ctypes.byref(d), FAKE, FAKE, FAKE, None, None)] == "GDN_ERR_SHAPE"
+    d = dims()
+    assert gdn.STATUS[lib.gdn_tree_ancestors(ctypes.byref(d), None, FAKE, FAKE, None, None)] == "GDN_ERR_NULL"
+    assert gdn.STATUS[lib.gdn_tree_ancestors(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 4, None)] == "GDN_ERR_ALIGN"
+    assert lib.gdn_tree_ancestors(ctypes.byref(dims(B=0)), None, None, None, None, None) == 0
+
+
+def test_python_binding_has_no_cpu_fallback():
+    """the binding never imports the oracle and has no CPU compute path"""
+    src = open(os.path.join(ROOT, "gated_deltanet_tree_gdn_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("oracle is", "")
+    assert "numpy" not in src

@@ -1,0 +1,324 @@
+"""GPU parity: the HIP library (called through its C ABI) against the fp64
+oracle, element by element, on seeded inputs; plus the exactness and
+invariance properties of rollback-free tree verification.
+
+Bars (stated here, applied to every whole output tensor, o and S_new):
+  rel-L2 = ||x - y||_2 / ||y||_2 <= 1e-3   and   max |x - y| <= 5e-3,
+with y the fp64 oracle, on bf16 q/k/v and an fp32 state.  Ancestor sets,
+depths and the hand-worked dyadic example must match bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import gdn_inputs as G
+import oracle
+
+torch = pytest.importorskip("torch")
+gdn = pytest.importorskip("gated_deltanet_tree_gdn_amd")
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-3
+MAX_ABS = 5e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: GPU tests need an MI355X")
+    gdn.load_library()  # fails loudly if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def errors(x, y):
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    rel = np.linalg.norm(x - y) / max(np.linalg.norm(y), 1e-300)
+    mab = float(np.max(np.abs(x - y))) if x.size else 0.0
+    return rel, mab
+
+
+def assert_close(x, y, what):
+    rel, mab = errors(x, y)
+    say(f"  {what}: rel-L2 {rel:.3e}  max-abs {mab:.3e}")
+    assert rel <= REL_L2 and mab <= MAX_ABS, f"{what}: rel-L2 {rel:.3e} max-abs {mab:.3e}"
+
+
+def run_verify(d, ctx=None):
+    o, ctx = gdn.verify(d["q"], d["k"], d["v"], d["g"], d["beta"], d["parent"], d["S0"], ctx=ctx)
+    return o, ctx
+
+
+def case_inputs(name, **shrink):
+    cfg = G.CONFIGS[name]
+    if shrink:
+        cfg = G.shrink(cfg, **shrink)
+    inp = G.make_inputs(cfg, seed=0)
+    return cfg, inp, G.to_device(inp)
+
+
+# ----------------------------------------------------------------------------
+# parity on the workloads
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_f32", "chain64", "bestfirst128", "batched_commit", "bestfirst_b32n128"])
+def test_parity_workload(name):
+    cfg, inp, d = case_inputs(name)
+    say(f"[parity] {name}: B={cfg.B} N={cfg.N} Hk={cfg.H_k} Hv={cfg.H_v} d={cfg.d_k} {cfg.dtype}")
+    o, ctx = run_verify(d)
+    gdn.gdn_ctx_status(ctx)
+    want = oracle.verify_inputs(inp)
+    assert_close(o.cpu().numpy(), want, f"{name} o")
+    acc = inp.get("accepted")
+    if acc is None:
+        acc = G.rng_for(1).integers(-1, cfg.N, size=cfg.B).astype(np.int32)
+    S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
+    gdn.gdn_ctx_status(ctx)
+    assert_close(S_new.cpu().numpy(), oracle.commit_inputs(inp, accepted=acc), f"{name} S_new")
+
+
+def unit_from_device(d, parent, b, h):
+    """one (sequence, value head) unit of device inputs as fp64 host arrays"""
+    Hk, Hv = d["q"].shape[2], d["v"].shape[2]
+    kh = h // (Hv // Hk)
+
+    def host(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    return {"q": host(d["q"][b:b + 1, :, kh:kh + 1]), "k": host(d["k"][b:b + 1, :, kh:kh + 1]),
+            "v": host(d["v"][b:b + 1, :, h:h + 1]), "g": host(d["g"][b:b + 1, :, h:h + 1]),
+            "beta": host(d["beta"][b:b + 1, :, h:h + 1]), "S0": host(d["S0"][b:b + 1, h:h + 1]),
+            "parent": np.ascontiguousarray(parent[b:b + 1])}
+
+
+def test_parity_stress48_sampled():
+    """48 layers of B=64, N=256, 32 value / 16 key heads, best-first trees of
+    depth <= 24 shared by all layers: every layer verified on the GPU; all
+    heads of sequence 0 of layer 0 and two seeded (b, h) units of every other
+    layer checked against the oracle; commits sampled on layer 0."""
+    cfg = G.CONFIGS["stress48"]
+    parent = G.make_tree(cfg, G.rng_for(0, 0))
+    rng = G.rng_for(2)
+    ctx = None
+    for layer in range(cfg.layers):
+        d = G.make_inputs_device(cfg, seed=0, layer=layer, parent=parent)
+        if ctx is None:
+            ctx = gdn.GdnContext.for_tensors(d["q"], d["v"], d["parent"])
+        o, _ = run_verify(d, ctx=ctx)
+        gdn.gdn_ctx_status(ctx)
+        units = [(0, h) for h in range(cfg.H_v)] if layer == 0 else \
+            [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H_v))) for _ in range(2)]
+        say(f"[parity] stress48 layer {layer}: checking {len(units)} units")
+        got = [o[b, :, h].cpu().numpy() for b, h in units]
+        want = [oracle.verify_inputs(unit_from_device(d, parent, b, h))[0, :, 0] for b, h in units]
+        assert_close(np.stack(got), np.stack(want), f"stress48 layer {layer} sampled o")
+        if layer == 0:
+            acc = rng.integers(-1, cfg.N, size=cfg.B).astype(np.int32)
+            S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
+            gdn.gdn_ctx_status(ctx)
+            picks = [(0, 0), (0, 17), (5, 31), (int(np.argmax(acc)), 3)]
+            gotS = [S_new[b, h].cpu().numpy() for b, h in picks]
+            wantS = [oracle.commit_inputs(unit_from_device(d, parent, b, h), accepted=acc[b:b + 1])[0, 0]
+                     for b, h in picks]
+            assert_close(np.stack(gotS), np.stack(wantS), "stress48 layer 0 sampled S_new")
+        del d, o
+
+
+# ----------------------------------------------------------------------------
+# exact results
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("which", ["tree", "chain"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_dyadic_example_bit_exact(which, dtype, d):
+    from tests.conftest import read_golden
+    gold = read_golden("dyadic_tree3.txt")
+    say(f"[exact] dyadic {which} {dtype} d={d}")
+    N = 3
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    e0 = torch.zeros(d)
+    e0[0] = 1
+    q = e0.repeat(1, N, 1, 1).to(tdt).cuda().contiguous()
+    k = q.clone()
+    v = torch.zeros(1, N, 1, d)
+    v[0, :, 0, 0] = torch.tensor(gold["v"])
+    v = v.to(tdt).cuda().contiguous()
+    g = torch.full((1, N, 1), gold["g"][0]).cuda()
+    beta = torch.full((1, N, 1), gold["beta"][0]).cuda()
+    S0 = torch.zeros(1, 1, d, d)
+    S0[0, 0, 0, 0] = gold["S0"][0]
+    S0 = S0.cuda()
+    parent = torch.tensor([gold["parent_" + which]], dtype=torch.int32).cuda()
+    o, ctx = gdn.verify(q, k, v, g, beta, parent, S0)
+    want = torch.zeros(1, N, 1, d)
+    want[0, :, 0, 0] = torch.tensor(gold["o_" + which])
+    assert torch.equal(o.cpu(), want)
+    for a in range(N):
+        Sn = gdn.gdn_commit_path(ctx, torch.tensor([a], dtype=torch.int32).cuda())
+        wantS = torch.zeros(1, 1, d, d)
+        wantS[0, 0, 0, 0] = gold["commit_" + which][a]
+        assert torch.equal(Sn.cpu(), wantS)
+
+
+@pytest.mark.parametrize("N", [1, 5, 31, 32, 33, 100, 256])
+def test_ancestors_bit_exact(N):
+    rng = G.rng_for(N)
+    trees = [G.tree_uniform(rng, 2, N), G.tree_chain(1, N), G.tree_best_first(rng, 2, N, 24 if N > 100 else 8)]
+    forest = G.tree_uniform(rng, 1, N)
+    forest[0, rng.random(N) < 0.2] = -1
+    trees.append(forest)
+    parent = np.concatenate(trees).astype(np.int32)
+    say(f"[exact] ancestors B={parent.shape[0]} N={N}")
+    anc, depth, status = gdn.gdn_tree_ancestors(torch.from_numpy(parent).cuda())
+    want_anc, want_depth = oracle.ancestors(parent)
+    assert np.array_equal(anc.cpu().numpy().view(np.uint32), want_anc)
+    assert np.array_equal(depth.cpu().numpy(), want_depth)
+    assert not status.cpu().numpy().any()
+
+
+# ----------------------------------------------------------------------------
+# properties of rollback-free verification
+# ----------------------------------------------------------------------------
+
+def test_prefix_state_untouched_and_deterministic():
+    cfg, inp, d = case_inputs("bestfirst128")
+    say("[prop] S0 untouched, 10 calls bitwise identical")
+    S0_before = d["S0"].clone()
+    o1, ctx = run_verify(d)
+    for _ in range(9):
+        o2, _ = run_verify(d, ctx=ctx)
+        assert torch.equal(o1, o2)
+    assert torch.equal(d["S0"], S0_before)
+
+
+def test_subtree_locality_bitwise():
+    cfg, inp, d = case_inputs("bestfirst128", H_v=4, H_k=2)
+    par = inp["parent"][0]
+    anc, _ = oracle.ancestors(inp["parent"])
+    o1, ctx = run_verify(d)
+    for j in (0, 5, 40, 127):
+        say(f"[prop] perturb node {j}")
+        d2 = {n: t.clone() for n, t in d.items()}
+        d2["k"][0, j] = d2["k"][0, j].flip(-1)
+        d2["v"][0, j] *= -2
+        d2["g"][0, j] -= 0.3
+        d2["beta"][0, j] *= 0.5
+        o2, _ = run_verify(d2)
+        desc = np.array([(anc[0, i, j // 32] >> (j % 32)) & 1 for i in range(cfg.N)], bool)
+        same = (o1 == o2).reshape(cfg.N, -1).all(dim=1).cpu().numpy()
+        assert np.array_equal(same, ~desc)
+
+
+def test_commit_in_place_and_off_path_invariance():
+    cfg, inp, d = case_inputs("batched_commit", B=4)
+    acc = torch.from_numpy(inp["accepted"][:4]).cuda()
+    o, ctx = run_verify(d)
+    S_out = gdn.gdn_commit_path(ctx, acc)
+    S_copy = d["S0"].clone()
+    o2, ctx2 = run_verify(dict(d, S0=S_copy))
+    gdn.gdn_commit_path(ctx2, acc, S_new=S_copy)  # in place
+    say("[prop] in-place commit")
+    assert torch.equal(S_copy, S_out)
+    # nodes off every accepted path: perturb them, the commit is unchanged
+    anc, _ = oracle.ancestors(inp["parent"][:4])
+    d3 = {n: t.clone() for n, t in d.items()}
+    for b in range(4):
+        a = int(inp["accepted"][b])
+        for j in range(cfg.N):
+            if not (anc[b, a, j // 32] >> (j % 32)) & 1:
+                d3["v"][b, j] += 1.0
+                d3["k"][b, j] = d3["k"][b, j].flip(-1)
+                d3["g"][b, j] -= 0.5
+    o3, ctx3 = run_verify(d3)
+    assert torch.equal(gdn.gdn_commit_path(ctx3, acc), S_out)
+
+
+def test_relabelled_tree_permutes_outputs():
+    cfg, inp, d = case_inputs("bestfirst128", H_v=4, H_k=2)
+    par = inp["parent"][0]
+    rng = G.rng_for(9)
+    placed, order = set(), []
+    while len(order) < cfg.N:
+        ready = [i for i in range(cfg.N) if i not in placed and (par[i] < 0 or par[i] in placed)]
+        pick = ready[rng.integers(len(ready))]
+        order.append(pick)
+        placed.add(pick)
+    new_of = {old: new for new, old in enumerate(order)}
+    perm = torch.tensor(order).cuda()
+    d2 = {n: d[n][:, perm].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    d2["S0"] = d["S0"]
+    d2["parent"] = torch.tensor([[new_of[par[o]] if par[o] >= 0 else -1 for o in order]], dtype=torch.int32).cuda()
+    o1, _ = run_verify(d)
+    o2, _ = run_verify(d2)
+    say("[prop] relabelled tree")
+    assert_close(o2.cpu().numpy(), o1[:, perm].cpu().numpy(), "relabelled o")
+
+
+# ----------------------------------------------------------------------------
+# edge cases
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [
+    dict(N=1), dict(N=37), dict(N=100, max_depth=40), dict(N=256, max_depth=24), dict(N=256, tree="chain"),
+    dict(d_k=64, d_v=64), dict(d_k=64, d_v=128), dict(d_k=128, d_v=64), dict(H_k=2, H_v=8),
+    dict(N=33, tree="uniform"), dict(dtype="f32", N=70),
+])
+def test_edge_shapes(shape):
+    base = G.shrink(G.CONFIGS["bestfirst128"], B=2, H_k=2, H_v=4)
+    cfg = G.shrink(base, **shape)
+    inp = G.make_inputs(cfg, seed=3)
+    say(f"[edge] {shape}")
+    d = G.to_device(inp)
+    o, ctx = run_verify(d)
+    gdn.gdn_ctx_status(ctx)
+    assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), f"edge {shape} o")
+    acc = np.array([cfg.N - 1, -1], np.int32)
+    S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
+    assert_close(S_new.cpu().numpy(), oracle.commit_inputs(inp, accepted=acc), f"edge {shape} S_new")
+
+
+def test_forest():
+    cfg = G.shrink(G.CONFIGS["bestfirst128"], B=2, H_k=1, H_v=2, N=64)
+    inp = G.make_inputs(cfg, seed=4)
+    inp["parent"][:, [10, 20, 33]] = -1
+    say("[edge] forest")
+    d = G.to_device(inp)
+    o, ctx = run_verify(d)
+    assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), "forest o")
+
+
+def test_empty_tree_is_noop():
+    cfg = G.shrink(G.CONFIGS["bestfirst128"], B=2, H_k=1, H_v=1, N=0)
+    inp = G.make_inputs(cfg)
+    d = G.to_device(inp)
+    o, ctx = run_verify(d)
+    assert o.shape == (2, 0, 1, 128)
+
+
+def test_invalid_tree_and_accepted_are_flagged():
+    cfg, inp, d = case_inputs("bestfirst128", B=3, H_k=1, H_v=2, N=40)
+    d["parent"][1, 7] = 9   # a forward edge
+    d["parent"][2, 3] = -5
+    say("[err] invalid tree")
+    o, ctx = run_verify(d)
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.gdn_ctx_status(ctx)
+    assert ei.value.status == "GDN_ERR_TREE"
+    cfg, inp, d = case_inputs("bestfirst128", B=3, H_k=1, H_v=2, N=40)
+    o, ctx = run_verify(d)
+    gdn.gdn_ctx_status(ctx)
+    say("[err] invalid accepted")
+    gdn.gdn_commit_path(ctx, torch.tensor([3, 40, -1], dtype=torch.int32).cuda())
+    with pytest.raises(gdn.GdnError) as ei:
+        gdn.gdn_ctx_status(ctx)
+    assert ei.value.status == "GDN_ERR_ACCEPT"
+    _, _, status = gdn.gdn_tree_ancestors(torch.tensor([[-1, 0, 5, 1]], dtype=torch.int32).cuda())
+    assert status.cpu().tolist() == [6]
