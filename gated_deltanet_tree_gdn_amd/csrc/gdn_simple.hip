@@ -1,38 +1,23 @@
-// gdn_simple.hip -- straightforward gfx950 kernels for GDN tree verification.
+// gdn_simple.hip -- straightforward gfx950 kernels for GDN tree verification:
+// the general verify path (any dtype, d in {64, 128}, N <= 256), the
+// accepted-path commit and the ancestor-set export.
 //
-// One 64-lane wavefront per (sequence b, value head h, 64-column slice of
-// d_v); lane c owns value column c.  Nodes are visited in topological
-// order; for node i the kernel walks the parent chain and applies
-//
-//   u_i = beta_i (v_i - gamma_i S0 k_i) - beta_i sum_{s in P°(i)} D_is (k_i.k_s) u_s
-//   o_i = gamma_i S0 q_i + sum_{s in P(i)} D_is (q_i.k_s) u_s
-//
-// with G_i the path-cumulative log-gate, gamma_i = exp(G_i) and
-// D_is = exp(G_i - G_s): the per-node form of the masked triangular solve
-// (I + X) U = beta (V - gamma K S0^T), O = gamma Q S0^T + Y U that the
-// Trees from Marginals technical summary describes (Methodology,
-// "3. Rollback-Free Tree Verification for GDN").  Only ancestor pairs are
-// ever touched, so masked entries are exact zeros by construction.
-//
-// These kernels are the general path: any dtype, d in {64, 128}, N <= 256.
+// Verify: one 64-lane wavefront per (sequence b, value head h, 64-column
+// slice of d_v) running the per-node walk of gdn_walk.h.
+// Commit: the same per-node update restricted to the root-to-accepted path,
+// then S_new = gamma_a S0 + sum_{s on the path} D_as u_s k_s^T (the delayed
+// state commitment of the Trees from Marginals technical summary, Methodology,
+// "3. Rollback-Free Tree Verification for GDN").
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "gdn_internal.h"
+#include "gdn_walk.h"
 
 namespace gdn {
 namespace {
-
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
 
 // Loads parent[b][:] into LDS, replacing any entry outside [-1, i-1] by -1
 // (so every parent walk terminates in bounds); returns 1 if one was invalid.
@@ -54,18 +39,15 @@ __device__ int load_parents(const int32_t* __restrict__ parent, int N, int* par_
 
 template <typename T, int DK>
 __global__ __launch_bounds__(64) void verify_simple_kernel(VerifyArgs a) {
-    const int N = a.N, Hv = a.H_v, Hk = a.H_k, DV = a.d_v;
-    const int nslice = DV / 64;
+    const int N = a.N, Hv = a.H_v;
+    const int nslice = a.d_v / 64;
     int blk = blockIdx.x;
     const int slice = blk % nslice;
     blk /= nslice;
     const int h = blk % Hv;
     const int b = blk / Hv;
-    const int kh = h / (Hv / Hk);
-    const int lane = threadIdx.x;
-    const int c = slice * 64 + lane;
 
-    __shared__ float u_s[kMaxN][64];
+    __shared__ float u_s[kMaxN * 64];
     __shared__ float G_s[kMaxN];
     __shared__ int par_s[kMaxN];
     __shared__ float ki_s[DK];
@@ -73,72 +55,8 @@ __global__ __launch_bounds__(64) void verify_simple_kernel(VerifyArgs a) {
     __shared__ int bad_s;
 
     const int bad = load_parents(a.parent + static_cast<size_t>(b) * N, N, par_s, &bad_s);
-    if (h == 0 && slice == 0 && lane == 0) a.tree_status[b] = bad ? GDN_ERR_TREE : 0;
-
-    const T* __restrict__ q = static_cast<const T*>(a.q);
-    const T* __restrict__ k = static_cast<const T*>(a.k);
-    const T* __restrict__ v = static_cast<const T*>(a.v);
-
-    float srow[DK];
-    {
-        const float4* src = reinterpret_cast<const float4*>(a.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + c) * DK);
-#pragma unroll
-        for (int j = 0; j < DK / 4; ++j) {
-            float4 t = src[j];
-            srow[4 * j + 0] = t.x;
-            srow[4 * j + 1] = t.y;
-            srow[4 * j + 2] = t.z;
-            srow[4 * j + 3] = t.w;
-        }
-    }
-
-    for (int i = 0; i < N; ++i) {
-        const int p = par_s[i];
-        const size_t nh = (static_cast<size_t>(b) * N + i) * Hv + h;
-        const float gi = a.g[nh];
-        const float bi = a.beta[nh];
-        const float Gi = (p < 0 ? 0.f : G_s[p]) + gi;
-        const size_t krow = ((static_cast<size_t>(b) * N + i) * Hk + kh) * DK;
-        for (int j = lane; j < DK; j += 64) {
-            ki_s[j] = to_f32(k[krow + j]);
-            qi_s[j] = to_f32(q[krow + j]);
-        }
-        __syncthreads();
-        if (lane == 0) G_s[i] = Gi;
-
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int j = 0; j < DK; ++j) {
-            sk += srow[j] * ki_s[j];
-            sq += srow[j] * qi_s[j];
-        }
-        float self_qk = 0.f;
-        for (int j = lane; j < DK; j += 64) self_qk += qi_s[j] * ki_s[j];
-        self_qk = wave_sum(self_qk);
-
-        float acc_u = 0.f, acc_o = 0.f;
-        for (int s = p; s >= 0; s = par_s[s]) {
-            const size_t srow_k = ((static_cast<size_t>(b) * N + s) * Hk + kh) * DK;
-            float pk = 0.f, pq = 0.f;
-            for (int j = lane; j < DK; j += 64) {
-                const float ks = to_f32(k[srow_k + j]);
-                pk += ki_s[j] * ks;
-                pq += qi_s[j] * ks;
-            }
-            pk = wave_sum(pk);
-            pq = wave_sum(pq);
-            const float D = __expf(Gi - G_s[s]);
-            const float us = u_s[s][lane];
-            acc_u += D * pk * us;
-            acc_o += D * pq * us;
-        }
-        const float gam = __expf(Gi);
-        const float vi = to_f32(v[nh * DV + c]);
-        const float ui = bi * (vi - gam * sk - acc_u);
-        u_s[i][lane] = ui;
-        a.o[nh * DV + c] = gam * sq + acc_o + self_qk * ui;
-        __syncthreads();
-    }
+    if (h == 0 && slice == 0 && threadIdx.x == 0) a.tree_status[b] = bad ? GDN_ERR_TREE : 0;
+    walk_verify_slice<T, DK, BlockSync>(a, b, h, slice * 64, par_s, u_s, G_s, ki_s, qi_s);
 }
 
 template <typename T, int DK>
@@ -315,6 +233,5 @@ hipError_t launch_ancestors(int B, int N, const int32_t* parent, uint32_t* anc, 
     return hipGetLastError();
 }
 
-hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) { return launch_verify_simple(a, stream); }
 
 }  // namespace gdn

@@ -42,6 +42,9 @@
  *    whose tree or accepted node is invalid are unspecified (but every
  *    access stays in bounds).
  *  - Non-finite inputs propagate; they are not checked.
+ *  - GDN_FORCE_SIMPLE=1 (read when a context is created) routes that
+ *    context's verify to the per-node walk kernels instead of the MFMA path
+ *    (for A/B comparison; results agree within the stated tolerance).
  *  - Calls are asynchronous on `stream` (NULL = the default stream) and
  *    complete in stream order.
  */

@@ -270,6 +270,7 @@ def test_relabelled_tree_permutes_outputs():
     dict(N=1), dict(N=37), dict(N=100, max_depth=40), dict(N=256, max_depth=24), dict(N=256, tree="chain"),
     dict(d_k=64, d_v=64), dict(d_k=64, d_v=128), dict(d_k=128, d_v=64), dict(H_k=2, H_v=8),
     dict(N=33, tree="uniform"), dict(dtype="f32", N=70),
+    dict(N=64, tree="chain"), dict(N=128, tree="chain"), dict(N=200, tree="uniform"),
 ])
 def test_edge_shapes(shape):
     base = G.shrink(G.CONFIGS["bestfirst128"], B=2, H_k=2, H_v=4)
@@ -322,3 +323,14 @@ def test_invalid_tree_and_accepted_are_flagged():
     assert ei.value.status == "GDN_ERR_ACCEPT"
     _, _, status = gdn.gdn_tree_ancestors(torch.tensor([[-1, 0, 5, 1]], dtype=torch.int32).cuda())
     assert status.cpu().tolist() == [6]
+
+
+@pytest.mark.parametrize("name", ["chain64", "bestfirst128", "batched_commit"])
+def test_walk_kernels_parity(name, monkeypatch):
+    """the per-node walk kernels (GDN_FORCE_SIMPLE=1) on bf16 inputs"""
+    monkeypatch.setenv("GDN_FORCE_SIMPLE", "1")
+    cfg, inp, d = case_inputs(name, B=min(G.CONFIGS[name].B, 4))
+    say(f"[walk] {name}")
+    o, ctx = run_verify(d)
+    gdn.gdn_ctx_status(ctx)
+    assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), f"walk {name} o")
