@@ -15,23 +15,28 @@
 // back-substitution along the root-to-i path, z_b = Y_{i,t_b} -
 // sum_{a>b} z_a X_{t_a,t_b}, which needs only the pairs (node, ancestor).
 //
-// Work decomposition: one workgroup per (sequence, value head), d_v/32
-// wavefronts; wavefront w owns value columns [32w, 32w + 32) as two 16-wide
-// MFMA tiles and keeps its slice of S0 (as a bf16 hi + lo pair), and R', in
-// registers.  K is staged in LDS (read by every wavefront); Q rows are read
-// straight from global memory.  Dense contractions run on
-// v_mfma_f32_16x16x32_bf16: q and k are exact bf16, S0, R' and Z~ are split
-// into hi + lo bf16 so products stay near fp32 accuracy.
+// Work decomposition: a persistent grid, one workgroup per compute unit,
+// each walking a contiguous run of (sequence, value head) items in head
+// order.  Consecutive items of one sequence share the tree structure
+// (depth, root paths, ancestor bits); the value heads of one key head also
+// share the staged K and Q and their Gram values.  d_v/16 wavefronts; the
+// wavefront w owns value columns [16w, 16w + 16) (one MFMA tile) and keeps
+// its slice of S0 (as a bf16 hi + lo pair) and R' in registers.  Dense
+// contractions run on v_mfma_f32_16x16x32_bf16: q and k are exact bf16; S0,
+// R' and Z~ are split into hi + lo bf16 so products stay near fp32 accuracy.
 //
-// Phases: (1) issue the S0 and K loads; (2) parents, depth by pointer
-// jumping, offsets of each node's path in a pair list; (3) pair Gram values
-// (MFMA over the lower 16x16 tiles that contain ancestor pairs, scattered
-// into the pair list); (4) G, gamma, X, Y and the rows of Z~, one thread per
-// node; (5) per wavefront: K S0^T -> R', then per 16-row tile Q S0^T and
-// Z~ R' -> o.
+// Per item: (1) S0 and V loads for this item are issued first, and the node
+// scalars and K/Q of the next item are prefetched into registers during this
+// one, so the memory system is not idle between items; (2) for a new
+// sequence: depth and root paths (pointer jumping, prefix sum), ancestor
+// bits; (3) for a new key head: K, Q into LDS and the Gram values of the
+// ancestor pairs (MFMA over the lower 16x16 tiles holding pairs); (4) G,
+// gamma, X, Y, the rows of Z~ (one thread per node) scattered into ready
+// MFMA A fragments; (5) per wavefront: K S0^T -> R', then per 16-row tile
+// Q S0^T and Z~ R' -> o.
 //
-// Trees whose pair list exceeds the LDS budget fall back, inside the same
-// workgroup, to the per-node walk of gdn_walk.h.
+// Trees whose pair list exceeds the LDS budget are verified, inside the same
+// workgroup, by the per-node walk of gdn_walk.h.
 
 #include <hip/hip_runtime.h>
 
@@ -39,6 +44,13 @@
 
 #include "gdn_internal.h"
 #include "gdn_walk.h"
+
+// Phase markers: no-ops here; a profiling build defines them to accumulate
+// per-phase cycle counts.
+#ifndef GDN_PHASE
+#define GDN_PHASE_INIT
+#define GDN_PHASE(k)
+#endif
 
 namespace gdn {
 namespace {
@@ -58,13 +70,6 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& 
         hi[j] = h;
         lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
     }
-}
-
-__device__ __forceinline__ bf16x8 zero_frag() {
-    bf16x8 z;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) z[j] = static_cast<__bf16>(0.f);
-    return z;
 }
 
 __device__ __forceinline__ bf16x8 load_frag(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -91,19 +96,25 @@ struct Lds {
     static constexpr int KROW = DK * 2 + 16;    // staged k / q row, padded against bank conflicts
     static constexpr int KS_OFF = 0;
     static constexpr int QS_OFF = NMAX * KROW;
-    static constexpr int ZD = QS_OFF + (DENSE ? NMAX * KROW : 0);      // Z~ fragment blocks (hi 1 KiB + lo 1 KiB)
+    static constexpr int ZD = QS_OFF + (DENSE ? NMAX * KROW : 0);  // Z~ fragment blocks (hi 1 KiB + lo 1 KiB)
     static constexpr int ZD_BYTES = DENSE ? 2048 * zblocks_before(NMAX / 16) : 0;
-    static constexpr int XC = ZD + ZD_BYTES;    // float[CAP]: k.k, then X
-    static constexpr int YC = XC + 4 * CAP;     // float[CAP]: q.k, then Y
-    static constexpr int ZC = YC + 4 * CAP;     // float[CAP]: rows of Z~
-    static constexpr int OFP = ZC + 4 * CAP;    // uint16[CAP]: path offset of the ancestor
+    // For NMAX <= 128 the Gram values of a key head are kept for its other
+    // value heads; larger trees recompute them per value head in place.
+    static constexpr bool KEEP_GRAM = DENSE;
+    static constexpr int KK = ZD + ZD_BYTES;    // float[CAP]: k_i . k_s of every pair (per key head)
+    static constexpr int QK = KK + (KEEP_GRAM ? 4 * CAP : 0);  // float[CAP]: q_i . k_s
+    static constexpr int XC = QK + (KEEP_GRAM ? 4 * CAP : 0);  // float[CAP]: X (per value head)
+    static constexpr int YC = XC + 4 * (CAP + 16);  // float[CAP]: Y, then the rows of Z~ (X has 16 zero pads)
+    static constexpr int OFP = YC + 4 * CAP;    // uint16[CAP]: path offset of the ancestor
     static constexpr int PATH = OFP + 2 * CAP;  // uint8[CAP]: root..i path of every node
-    static constexpr int NODE = (PATH + CAP + 15) & ~15;
+    static constexpr int PNODE = PATH + CAP;    // uint8[CAP]: node owning each pair
+    static constexpr int NODE = (PNODE + CAP + 15) & ~15;
     static constexpr int PAR = NODE;            // int[NMAX]
     static constexpr int DEP = PAR + 4 * NMAX;
     static constexpr int OFF = DEP + 4 * NMAX;
     static constexpr int NXT = OFF + 4 * NMAX;
-    static constexpr int BET = NXT + 4 * NMAX;  // float[NMAX]: beta
+    static constexpr int GV = NXT + 4 * NMAX;   // float[NMAX]: g of the item's head
+    static constexpr int BET = GV + 4 * NMAX;   // beta
     static constexpr int GG = BET + 4 * NMAX;   // G (path sum of g)
     static constexpr int GAM = GG + 4 * NMAX;   // gamma (0 past N)
     static constexpr int ANC = GAM + 4 * NMAX;  // uint32[NMAX][AW]: ancestor bit rows
@@ -114,13 +125,16 @@ struct Lds {
     static_assert(NMAX * 64 * 4 + DK * 64 * 4 <= NODE, "fallback u and S0 buffers must fit below the node arrays");
 };
 
-// One wavefront owns 16 value columns (one MFMA tile): column 16 w + lc.
+// Four wavefronts; wavefront w owns CT = d_v / 64 MFMA tiles of 16 value
+// columns.  With CT = 2 a lane's two columns are adjacent (32 w + 2 lc + st),
+// so V is read in 4-byte and o written in 8-byte pieces.
 template <int NMAX, int DK, int DV>
-__global__ __launch_bounds__(64 * (DV / 16)) void verify_fast_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int items_per_wg) {
     using L = Lds<NMAX, DK>;
     constexpr bool DENSE = L::DENSE;
-    constexpr int NW = DV / 16;         // wavefronts
+    constexpr int NW = 4;               // wavefronts
     constexpr int NTH = 64 * NW;        // threads
+    constexpr int CT = DV / 64;         // 16-column MFMA tiles per wavefront
     constexpr int KS = DK / 32;         // MFMA k-steps over d_k
     constexpr int NTMAX = NMAX / 16;    // 16-row tiles
     constexpr int NKMAX = NMAX / 32;    // 32-node k-steps over the tree
@@ -131,25 +145,15 @@ __global__ __launch_bounds__(64 * (DV / 16)) void verify_fast_kernel(VerifyArgs 
 
     __shared__ __align__(16) unsigned char smem[L::TOTAL];
 
-    // ---- which (sequence, value head): the value heads sharing a key head
-    // sit 8 blocks apart, so they land on the same XCD and share its L2.
-    const int R = a.H_v / a.H_k;
-    const int Lb = blockIdx.x;
-    const int rem = Lb % (8 * R);
-    const int grp = (Lb / (8 * R)) * 8 + (rem & 7);
-    if (grp >= a.B * a.H_k) return;
-    const int r = rem >> 3;
-    const int b = grp / a.H_k;
-    const int kh = grp % a.H_k;
-    const int h = kh * R + r;
-    const int N = a.N, Hk = a.H_k, Hv = a.H_v;
+    const int N0 = a.N, Hk = a.H_k, Hv = a.H_v;
+    const int R = Hv / Hk;
+    const int n_items = a.B * Hv;
+    const int it_begin = blockIdx.x * items_per_wg;
+    const int it_end = min(it_begin + items_per_wg, n_items);
+    if (it_begin >= it_end) return;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int lc = lane & 15;
-    const int lg = lane >> 4;
-    const int col = 16 * wave + lc;  // this lane's value column
+    const int tid0 = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
 
     const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
     const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
@@ -159,6 +163,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void verify_fast_kernel(VerifyArgs 
     int* dep = reinterpret_cast<int*>(smem + L::DEP);
     int* off = reinterpret_cast<int*>(smem + L::OFF);
     int* nxt = reinterpret_cast<int*>(smem + L::NXT);
+    float* gv = reinterpret_cast<float*>(smem + L::GV);
     float* bet = reinterpret_cast<float*>(smem + L::BET);
     float* Gs = reinterpret_cast<float*>(smem + L::GG);
     float* gam = reinterpret_cast<float*>(smem + L::GAM);
@@ -167,397 +172,617 @@ __global__ __launch_bounds__(64 * (DV / 16)) void verify_fast_kernel(VerifyArgs 
     int* misc = reinterpret_cast<int*>(smem + L::MISC);
     float* xc = reinterpret_cast<float*>(smem + L::XC);
     float* yc = reinterpret_cast<float*>(smem + L::YC);
-    float* zc = reinterpret_cast<float*>(smem + L::ZC);
+    float* kk = L::KEEP_GRAM ? reinterpret_cast<float*>(smem + L::KK) : xc;
+    float* qk = L::KEEP_GRAM ? reinterpret_cast<float*>(smem + L::QK) : yc;
     uint16_t* ofp = reinterpret_cast<uint16_t*>(smem + L::OFP);
     uint8_t* pathc = smem + L::PATH;
+    uint8_t* pnode = smem + L::PNODE;
     unsigned char* Ks = smem + L::KS_OFF;
     unsigned char* Qs = smem + L::QS_OFF;
     unsigned char* Zd = smem + L::ZD;
 
-    // ---- (1) every global load this workgroup needs, issued up front and
-    // unconditionally (indices clamped into range, out-of-range values
-    // replaced after the load) so they all fly during the prologue: node
-    // scalars, this wavefront's S0 rows (lane (lc, lg) holds d_k columns
-    // [8 KS lg, 8 KS (lg + 1)) of row `col`), its V column for every node,
-    // and a share of K and Q.
-    int p_in[IPT];
-    float g_in[IPT], b_in[IPT];
+    // Prefetched state of the next item: node scalars, and K/Q shares when
+    // it starts a new key head.  Loads are unconditional with indices
+    // clamped into range; out-of-range values are replaced after arrival.
+    int p_pf[IPT];
+    float g_pf[IPT], b_pf[IPT];
+    uint4 k_pf[KCH], q_pf[DENSE ? KCH : 1];
+    auto prefetch_scalars = [&](int it, int tid, int N) {
+        const int bb = it / Hv, hh = it % Hv;
 #pragma unroll
-    for (int q = 0; q < IPT; ++q) {
-        const int i = min(tid + q * NTH, N - 1);
-        p_in[q] = a.parent[static_cast<size_t>(b) * N + i];
-        const size_t nh = (static_cast<size_t>(b) * N + i) * Hv + h;
-        g_in[q] = a.g[nh];
-        b_in[q] = a.beta[nh];
-    }
-    // keep the node scalars ahead of the bulk loads: the prologue waits on
-    // them only
-    __builtin_amdgcn_sched_barrier(0);
-    float4 s0r[2 * KS];
-    {
-        const float4* src = reinterpret_cast<const float4*>(a.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + col) * DK + 8 * KS * lg);
-#pragma unroll
-        for (int q = 0; q < 2 * KS; ++q) s0r[q] = src[q];
-    }
-    uint4 kraw[KCH], qraw[DENSE ? KCH : 1];
-#pragma unroll
-    for (int q = 0; q < KCH; ++q) {
-        const int e = tid + q * NTH;
-        const int row = min(e / (DK / 8), N - 1);
-        const size_t gofs = ((static_cast<size_t>(b) * N + row) * Hk + kh) * DK + (e % (DK / 8)) * 8;
-        kraw[q] = *reinterpret_cast<const uint4*>(kg + gofs);
-        if (DENSE) qraw[q] = *reinterpret_cast<const uint4*>(qg + gofs);
-    }
-    const size_t vbase = static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV + col;
-    uint16_t vraw[NTMAX][4];
-#pragma unroll
-    for (int S = 0; S < NTMAX; ++S)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) vraw[S][rr] = vg[vbase + static_cast<size_t>(min(16 * S + 4 * lg + rr, N - 1)) * Hv * DV];
-
-    // ---- (2) parents (invalid entries become -1 so every walk ends); depth
-    // and the path sum G of g by pointer jumping: dep[i] counts the nodes and
-    // Gs[i] sums g from i up to (excluding) nxt[i].
-    int bad_local = 0;
-#pragma unroll
-    for (int q = 0; q < IPT; ++q) {
-        const int i = tid + q * NTH;
-        if (i < NMAX) {
-            int p = i < N ? p_in[q] : -1;
-            if (p < -1 || p >= i) {
-                bad_local = 1;
-                p = -1;
-            }
-            par[i] = p;
-            nxt[i] = p;
-            dep[i] = i < N ? 1 : 0;
-            Gs[i] = i < N ? g_in[q] : 0.f;
-            bet[i] = i < N ? b_in[q] : 0.f;
+        for (int q = 0; q < IPT; ++q) {
+            const int i = min(tid + q * NTH, N - 1);
+            p_pf[q] = a.parent[static_cast<size_t>(bb) * N + i];
+            const size_t nh = (static_cast<size_t>(bb) * N + i) * Hv + hh;
+            g_pf[q] = a.g[nh];
+            b_pf[q] = a.beta[nh];
         }
-    }
-    if (tid < NMAX / 16) tmask[tid] = 0u;
-    if (DENSE)
-        for (int e = tid; e < L::ZD_BYTES / 16; e += NTH) reinterpret_cast<uint4*>(Zd)[e] = make_uint4(0u, 0u, 0u, 0u);
-    const int bad = __syncthreads_or(bad_local);
-    if (kh == 0 && r == 0 && tid == 0) a.tree_status[b] = bad ? GDN_ERR_TREE : 0;
+    };
+    auto prefetch_kq = [&](int it, int tid, int N) {
+        const int bb = it / Hv, kh = (it % Hv) / R;
+#pragma unroll
+        for (int q = 0; q < KCH; ++q) {
+            const int e = tid + q * NTH;
+            const int row = min(e / (DK / 8), N - 1);
+            const size_t gofs = ((static_cast<size_t>(bb) * N + row) * Hk + kh) * DK + (e % (DK / 8)) * 8;
+            k_pf[q] = *reinterpret_cast<const uint4*>(kg + gofs);
+            if (DENSE) q_pf[q] = *reinterpret_cast<const uint4*>(qg + gofs);
+        }
+    };
+    GDN_PHASE_INIT;
+    prefetch_scalars(it_begin, tid0, N0);
+    __builtin_amdgcn_sched_barrier(0);
+    prefetch_kq(it_begin, tid0, N0);
 
-    for (int round = 0; round < 9; ++round) {
-        int c2[IPT], n2[IPT];
-        float G2[IPT];
-        int live = 0;
+    // k_pf/q_pf hold the K/Q of the first item; afterwards the K/Q of the
+    // next item are written into LDS at the end of the current one
+    bool kq_staged = false;
+    int cur_b = -1, cur_kh = -1, total = 0;
+    for (int it = it_begin; it < it_end; ++it) {
+        // Opaque copies of the thread index and N: everything derived from
+        // them is recomputed per item instead of being hoisted out of the
+        // loop and held in registers across it.
+        int tid = tid0, N = N0;
+        asm volatile("" : "+v"(tid));
+        asm volatile("" : "+s"(N));
+        const int lane = tid & 63;
+        const int lc = lane & 15;
+        const int lg = lane >> 4;
+        // value column of (lane, tile st)
+        auto column = [&](int st) { return CT == 1 ? 16 * wave + lc : 32 * wave + 2 * lc + st; };
+        const int b = it / Hv, h = it % Hv, kh = h / R;
+        const bool new_b = b != cur_b;
+        const bool new_kh = new_b || kh != cur_kh;
+        const bool do_gram = new_kh || !L::KEEP_GRAM;
+        const int nit = it + 1 < it_end ? it + 1 : -1;
+        const bool next_new_kh = nit >= 0 && (nit / Hv != b || (nit % Hv) / R != kh);
+        GDN_PHASE(0);
+
+        // ---- (1) this item's S0 rows (lane (lc, lg) of tile st holds d_k
+        // columns [8 KS lg, 8 KS (lg + 1)) of row column(st)) and V columns
+        // for every node, in flight during the tree work
+        float4 s0r[CT][2 * KS];
+#pragma unroll
+        for (int st = 0; st < CT; ++st) {
+            const float4* src =
+                reinterpret_cast<const float4*>(a.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + column(st)) * DK + 8 * KS * lg);
+#pragma unroll
+            for (int q = 0; q < 2 * KS; ++q) s0r[st][q] = src[q];
+        }
+        const size_t vbase = static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV + column(0);
+        uint32_t vraw[NTMAX][4];  // CT == 2: the lane's two adjacent bf16 columns
+#pragma unroll
+        for (int S = 0; S < NTMAX; ++S)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const uint16_t* vp = vg + vbase + static_cast<size_t>(min(16 * S + 4 * lg + rr, N - 1)) * Hv * DV;
+                vraw[S][rr] = CT == 1 ? static_cast<uint32_t>(*vp) : *reinterpret_cast<const uint32_t*>(vp);
+            }
+
+        // ---- (2) node scalars; for a new sequence the tree structure
+        int bad_local = 0;
 #pragma unroll
         for (int q = 0; q < IPT; ++q) {
             const int i = tid + q * NTH;
-            c2[q] = 0;
-            n2[q] = -1;
-            G2[q] = 0.f;
             if (i < NMAX) {
-                const int nx = nxt[i];
-                c2[q] = dep[i] + (nx >= 0 ? dep[nx] : 0);
-                G2[q] = Gs[i] + (nx >= 0 ? Gs[nx] : 0.f);
-                n2[q] = nx >= 0 ? nxt[nx] : -1;
-                live |= n2[q] >= 0;
+                gv[i] = i < N ? g_pf[q] : 0.f;
+                bet[i] = i < N ? b_pf[q] : 0.f;
+                if (new_b) {
+                    int p = i < N ? p_pf[q] : -1;
+                    if (p < -1 || p >= i) {
+                        bad_local = 1;
+                        p = -1;
+                    }
+                    par[i] = p;
+                    nxt[i] = p;
+                    dep[i] = i < N ? 1 : 0;
+                }
+            }
+        }
+        if (DENSE)
+            for (int e = tid; e < L::ZD_BYTES / 16; e += NTH) reinterpret_cast<uint4*>(Zd)[e] = make_uint4(0u, 0u, 0u, 0u);
+        if (nit >= 0) prefetch_scalars(nit, tid, N);
+        if (new_b) {
+            if (tid < NMAX / 16) tmask[tid] = 0u;
+            const int bad = __syncthreads_or(bad_local);
+            if (h == 0 && tid == 0) a.tree_status[b] = bad ? GDN_ERR_TREE : 0;
+            // depth by pointer jumping: dep[i] counts the nodes from i up to nxt[i]
+            for (int round = 0; round < 9; ++round) {
+                int c2[IPT], n2[IPT];
+                int live = 0;
+#pragma unroll
+                for (int q = 0; q < IPT; ++q) {
+                    const int i = tid + q * NTH;
+                    c2[q] = 0;
+                    n2[q] = -1;
+                    if (i < NMAX) {
+                        const int nx = nxt[i];
+                        c2[q] = dep[i] + (nx >= 0 ? dep[nx] : 0);
+                        n2[q] = nx >= 0 ? nxt[nx] : -1;
+                        live |= n2[q] >= 0;
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < IPT; ++q) {
+                    const int i = tid + q * NTH;
+                    if (i < NMAX) {
+                        dep[i] = c2[q];
+                        nxt[i] = n2[q];
+                    }
+                }
+                if (!__syncthreads_or(live)) break;
+            }
+            // offsets of each node's path in the pair list (exclusive scan)
+            if (wave == 0) {
+                constexpr int E = NMAX / 64;
+                int vals[E];
+                int sum = 0;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    vals[e] = dep[lane * E + e];
+                    sum += vals[e];
+                }
+                int incl = sum;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int t = __shfl_up(incl, o, 64);
+                    if (lane >= o) incl += t;
+                }
+                int run = incl - sum;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    off[lane * E + e] = run;
+                    run += vals[e];
+                }
+                if (lane == 63) misc[0] = incl;
+            }
+            __syncthreads();
+            total = misc[0];
+            if (total <= L::CAP) {
+                // root..i path, owner and ancestor offsets of every pair;
+                // ancestor bits; tiles holding pairs
+                for (int i = tid; i < NMAX; i += NTH) {
+                    uint32_t bits[L::AW];
+#pragma unroll
+                    for (int w = 0; w < L::AW; ++w) bits[w] = 0u;
+                    if (i < N) {
+                        int pos = off[i] + dep[i] - 1;
+                        uint32_t mask = 0u;
+                        for (int s = i; s >= 0; s = par[s]) {
+                            pathc[pos] = static_cast<uint8_t>(s);
+                            pnode[pos] = static_cast<uint8_t>(i);
+                            ofp[pos] = static_cast<uint16_t>(off[s]);
+                            --pos;
+                            mask |= 1u << (s >> 4);
+#pragma unroll
+                            for (int w = 0; w < L::AW; ++w) bits[w] |= (s >> 5) == w ? 1u << (s & 31) : 0u;
+                        }
+                        atomicOr(&tmask[i >> 4], mask);
+                    }
+#pragma unroll
+                    for (int w = 0; w < L::AW; ++w) anc[i * L::AW + w] = bits[w];
+                }
             }
         }
         __syncthreads();
-#pragma unroll
-        for (int q = 0; q < IPT; ++q) {
-            const int i = tid + q * NTH;
-            if (i < NMAX) {
-                dep[i] = c2[q];
-                Gs[i] = G2[q];
-                nxt[i] = n2[q];
+        GDN_PHASE(1);
+
+        if (total > L::CAP) {
+            // deep tree: the per-node walk by wavefront 0, one 64-column
+            // slice at a time; it overwrites the staged K/Q
+            if (wave == 0) {
+                float* u_s = reinterpret_cast<float*>(smem);
+                float* s0_s = reinterpret_cast<float*>(smem + NMAX * 64 * 4);
+                float* ki = reinterpret_cast<float*>(smem + L::FBKQ);
+                for (int c0 = 0; c0 < DV; c0 += 64)
+                    walk_verify_slice_lds<uint16_t, DK, WaveSync>(a, b, h, c0, par, u_s, Gs, ki, ki + DK, s0_s);
             }
+            if (next_new_kh) prefetch_kq(nit, tid, N);
+            kq_staged = false;
+            cur_b = b;
+            cur_kh = -1;
+            // this path leaves the S0 and V loads above unused: drain them
+            // here so the next item's loads into the same registers need no
+            // wait
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            continue;
         }
-        if (!__syncthreads_or(live)) break;
-    }
 
-    // offsets of each node's path in the pair list (exclusive scan of depth);
-    // gamma = exp(G)
-    if (wave == 0) {
-        constexpr int E = NMAX / 64;
-        int vals[E];
-        int sum = 0;
+        // ---- (3) new key head: K (and Q) into LDS (unless the previous item
+        // already put them there), rows past N zeroed; then the Gram values
+        // of the ancestor pairs
+        const int NT = (N + 15) >> 4;
+        auto q_frag = [&](int row, int ks) -> bf16x8 {
+            if (DENSE) return load_frag(Qs + row * L::KROW + 2 * (8 * KS * lg + 8 * ks));
+            return load_frag(qg + ((static_cast<size_t>(b) * N + min(row, N - 1)) * Hk + kh) * DK + 8 * KS * lg + 8 * ks);
+        };
+        auto k_frag = [&](int row, int ks) -> bf16x8 { return load_frag(Ks + row * L::KROW + 2 * (8 * KS * lg + 8 * ks)); };
+        auto stage_kq = [&]() {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            vals[e] = dep[lane * E + e];
-            sum += vals[e];
-        }
-        int incl = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int t = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += t;
-        }
-        int run = incl - sum;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            off[lane * E + e] = run;
-            run += vals[e];
-        }
-        if (lane == 63) misc[0] = incl;
-    }
-    for (int i = tid; i < NMAX; i += NTH) gam[i] = i < N ? __expf(Gs[i]) : 0.f;
-    __syncthreads();
-    const int total = misc[0];
-
-    if (total > L::CAP) {
-        // deep tree: the per-node walk, one wavefront, one 64-column slice at a time
-        if (wave != 0) return;
-        float* u_s = reinterpret_cast<float*>(smem);
-        float* s0_s = reinterpret_cast<float*>(smem + NMAX * 64 * 4);
-        float* ki = reinterpret_cast<float*>(smem + L::FBKQ);
-        for (int c0 = 0; c0 < DV; c0 += 64)
-            walk_verify_slice_lds<uint16_t, DK, WaveSync>(a, b, h, c0, par, u_s, Gs, ki, ki + DK, s0_s);
-        return;
-    }
-
-    // ---- K (and Q) into LDS (rows past N zeroed); root..i path, ancestor
-    // bits and the tiles holding pairs, per node
-#pragma unroll
-    for (int q = 0; q < KCH; ++q) {
-        const int e = tid + q * NTH;
-        const int row = e / (DK / 8);
-        const int cc = e % (DK / 8);
-        const uint32_t keep = row < N ? 0xFFFFFFFFu : 0u;  // rows past N become zeros
-        *reinterpret_cast<uint4*>(Ks + row * L::KROW + cc * 16) = mask4(kraw[q], keep);
-        if (DENSE) *reinterpret_cast<uint4*>(Qs + row * L::KROW + cc * 16) = mask4(qraw[q], keep);
-    }
-    for (int i = tid; i < NMAX; i += NTH) {
-        uint32_t bits[L::AW];
-#pragma unroll
-        for (int w = 0; w < L::AW; ++w) bits[w] = 0u;
-        if (i < N) {
-            int pos = off[i] + dep[i] - 1;
-            uint32_t mask = 0u;
-            for (int s = i; s >= 0; s = par[s]) {
-                pathc[pos] = static_cast<uint8_t>(s);
-                ofp[pos] = static_cast<uint16_t>(off[s]);
-                --pos;
-                mask |= 1u << (s >> 4);
-#pragma unroll
-                for (int w = 0; w < L::AW; ++w) bits[w] |= (s >> 5) == w ? 1u << (s & 31) : 0u;
+            for (int q = 0; q < KCH; ++q) {
+                const int e = tid + q * NTH;
+                const int row = e / (DK / 8);
+                const int cc = e % (DK / 8);
+                const uint32_t keep = row < N ? 0xFFFFFFFFu : 0u;
+                *reinterpret_cast<uint4*>(Ks + row * L::KROW + cc * 16) = mask4(k_pf[q], keep);
+                if (DENSE) *reinterpret_cast<uint4*>(Qs + row * L::KROW + cc * 16) = mask4(q_pf[q], keep);
             }
-            atomicOr(&tmask[i >> 4], mask);
+        };
+        if (new_kh && !kq_staged) {
+            stage_kq();
+            __syncthreads();
         }
+        if (do_gram) {
+            // lower 16x16 tiles holding pairs, dealt round-robin to the
+            // wavefronts; each value lands at its pair (i, s) = path position
+            // dep[s] - 1 of node i
+            int t = 0;
+            for (int I = 0; I < NT; ++I) {
+                const uint32_t tm = tmask[I];
+                for (int J = 0; J <= I; ++J) {
+                    if (!((tm >> J) & 1u)) continue;
+                    if (t++ % NW != wave) continue;
+                    f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < L::AW; ++w) anc[i * L::AW + w] = bits[w];
-    }
-    __syncthreads();
-
-    auto q_frag = [&](int row, int ks) -> bf16x8 {
-        if (DENSE) return load_frag(Qs + row * L::KROW + 2 * (8 * KS * lg + 8 * ks));
-        return load_frag(qg + ((static_cast<size_t>(b) * N + min(row, N - 1)) * Hk + kh) * DK + 8 * KS * lg + 8 * ks);
-    };
-    auto k_frag = [&](int row, int ks) -> bf16x8 { return load_frag(Ks + row * L::KROW + 2 * (8 * KS * lg + 8 * ks)); };
-
-    // ---- (3) Gram values of the ancestor pairs: the lower 16x16 tiles that
-    // hold pairs, dealt round-robin to the wavefronts; each value lands at
-    // its pair (i, s) = path position dep[s] - 1 of node i.
-    const int NT = (N + 15) >> 4;
-    {
-        int t = 0;
-        for (int I = 0; I < NT; ++I) {
-            const uint32_t tm = tmask[I];
-            for (int J = 0; J <= I; ++J) {
-                if (!((tm >> J) & 1u)) continue;
-                if (t++ % NW != wave) continue;
-                f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 kb = k_frag(16 * J + lc, ks);
+                        akk = mfma(k_frag(16 * I + lc, ks), kb, akk);
+                        aqk = mfma(q_frag(16 * I + lc, ks), kb, aqk);
+                    }
+                    const int s = 16 * J + lc;
+                    const int ds = dep[s];
+                    uint32_t aw[4];
+                    int oi[4];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 kb = k_frag(16 * J + lc, ks);
-                    akk = mfma(k_frag(16 * I + lc, ks), kb, akk);
-                    aqk = mfma(q_frag(16 * I + lc, ks), kb, aqk);
-                }
-                const int s = 16 * J + lc;
-                const int ds = dep[s];
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int i = 16 * I + 4 * lg + rr;
+                        aw[rr] = anc[i * L::AW + (s >> 5)];
+                        oi[rr] = off[i];
+                    }
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int i = 16 * I + 4 * lg + rr;
-                    const bool pair = i < N && ((anc[i * L::AW + (s >> 5)] >> (s & 31)) & 1u);
-                    if (pair) {
-                        const int p = off[i] + ds - 1;
-                        yc[p] = aqk[rr];
-                        if (s != i) xc[p] = akk[rr];
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const int i = 16 * I + 4 * lg + rr;
+                        if (i < N && ((aw[rr] >> (s & 31)) & 1u)) {
+                            const int p = oi[rr] + ds - 1;
+                            qk[p] = aqk[rr];
+                            kk[p] = akk[rr];
+                        }
                     }
                 }
             }
         }
-    }
-    __syncthreads();
 
-    // ---- (4) per node: X and Y on its pairs, then its row of Z~ by a
-    // right-looking sweep along its path (in registers for paths of up to
-    // ZR nodes), scaled by beta of the column's node
-    for (int i = tid; i < N; i += NTH) {
-        const int o = off[i], m = dep[i];
-        const float Gi = Gs[i], bi = bet[i];
-        for (int t = 0; t < m - 1; ++t) {
-            const float D = __expf(Gi - Gs[pathc[o + t]]);
-            xc[o + t] *= bi * D;
-            yc[o + t] *= D;
+        GDN_PHASE(2);
+        // ---- (4) G (path sum of g) and gamma per node; X and Y per pair;
+        // per node its row of Z~ by a right-looking sweep along its path (in
+        // registers for paths of up to ZR nodes), scaled by beta of the
+        // column's node and scattered into the A-fragment blocks
+        for (int i = tid; i < NMAX; i += NTH) {
+            float G = 0.f;
+            if (i < N) {
+                const int o = off[i], m = dep[i];
+                if (m <= ZR) {
+                    int t[ZR];
+#pragma unroll
+                    for (int bb = 0; bb < ZR; ++bb) t[bb] = pathc[o + min(bb, m - 1)];
+#pragma unroll
+                    for (int bb = 0; bb < ZR; ++bb) G += bb < m ? gv[t[bb]] : 0.f;
+                } else {
+                    for (int bb = 0; bb < m; ++bb) G += gv[pathc[o + bb]];
+                }
+            }
+            Gs[i] = G;
+            gam[i] = i < N ? __expf(G) : 0.f;
         }
-    }
-    __syncthreads();
-    for (int i = tid; i < N; i += NTH) {
-        const int o = off[i], m = dep[i];
-        if (m <= ZR) {
-            float z[ZR];
+        __syncthreads();
+        for (int p = tid; p < total; p += NTH) {
+            const int i = pnode[p], s = pathc[p];
+            const float D = __expf(Gs[i] - Gs[s]);
+            const float x = bet[i] * D * kk[p];
+            const float y = D * qk[p];
+            xc[p] = x;
+            yc[p] = y;
+        }
+        if (tid < 16) xc[total + tid] = 0.f;  // pads read by the branch-free solve below
+        __syncthreads();
+        for (int i = tid; i < N; i += NTH) {
+            const int o = off[i], m = dep[i];
+            if (m <= ZR) {
+                // branch-free: entries past the path are zero and their X
+                // reads land on finite values (pairs of later nodes or the
+                // zero pads), so loads can be issued early
+                int t[ZR], oa[ZR];
+                float z[ZR];
 #pragma unroll
-            for (int bb = 0; bb < ZR; ++bb) z[bb] = yc[o + min(bb, m - 1)];
+                for (int bb = 0; bb < ZR; ++bb) {
+                    const int pp = o + min(bb, m - 1);
+                    t[bb] = pathc[pp];
+                    oa[bb] = ofp[pp];
+                    z[bb] = bb < m ? yc[pp] : 0.f;
+                }
+                // one row of X in flight ahead of the row being applied
+                float xr[ZR - 1];
 #pragma unroll
-            for (int aa = ZR - 1; aa >= 1; --aa) {
-                if (aa < m) {
+                for (int bb = 0; bb < ZR - 1; ++bb) xr[bb] = xc[oa[ZR - 1] + bb];
+#pragma unroll
+                for (int aa = ZR - 1; aa >= 1; --aa) {
+                    float xn[ZR - 1];
+#pragma unroll
+                    for (int bb = 0; bb + 1 < aa; ++bb) xn[bb] = xc[oa[aa - 1] + bb];
                     const float za = z[aa];
-                    const int oa = ofp[o + aa];
 #pragma unroll
-                    for (int bb = 0; bb < aa; ++bb) z[bb] -= za * xc[oa + bb];
+                    for (int bb = 0; bb < aa; ++bb) z[bb] -= za * xr[bb];
+#pragma unroll
+                    for (int bb = 0; bb + 1 < aa; ++bb) xr[bb] = xn[bb];
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int bb = 0; bb < ZR; ++bb) z[bb] *= bet[t[bb]];
+                if (DENSE) {
+                    // block (I, kap) = rows 16I.., nodes 32kap..; node t sits in
+                    // lane group ((t >> 2) & 3), slot 4 ((t >> 4) & 1) + (t & 3)
+                    unsigned char* rowblk = Zd + 2048 * zblocks_before(i >> 4);
+#pragma unroll
+                    for (int bb = 0; bb < ZR; ++bb) {
+                        if (bb < m) {
+                            const int tt = t[bb];
+                            const __bf16 zh = static_cast<__bf16>(z[bb]);
+                            const __bf16 zl = static_cast<__bf16>(z[bb] - static_cast<float>(zh));
+                            const int e = (((((tt >> 2) & 3) << 4) | (i & 15)) << 3) + (((tt >> 4) & 1) << 2) + (tt & 3);
+                            unsigned char* blk = rowblk + 2048 * (tt >> 5);
+                            reinterpret_cast<__bf16*>(blk)[e] = zh;
+                            reinterpret_cast<__bf16*>(blk + 1024)[e] = zl;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int bb = 0; bb < ZR; ++bb)
+                        if (bb < m) yc[o + bb] = z[bb];
+                }
+                continue;
+            }
+            for (int aa = m - 1; aa >= 1; --aa) {
+                const float za = yc[o + aa];
+                const int oa = ofp[o + aa];
+                for (int bb = 0; bb < aa; ++bb) yc[o + bb] -= za * xc[oa + bb];
+            }
+            for (int bb = 0; bb < m; ++bb) yc[o + bb] *= bet[pathc[o + bb]];
+            if (DENSE) {
+                unsigned char* rowblk = Zd + 2048 * zblocks_before(i >> 4);
+                for (int bb = 0; bb < m; ++bb) {
+                    const int tt = pathc[o + bb];
+                    const float zz = yc[o + bb];
+                    const __bf16 zh = static_cast<__bf16>(zz);
+                    const __bf16 zl = static_cast<__bf16>(zz - static_cast<float>(zh));
+                    const int e = (((((tt >> 2) & 3) << 4) | (i & 15)) << 3) + (((tt >> 4) & 1) << 2) + (tt & 3);
+                    unsigned char* blk = rowblk + 2048 * (tt >> 5);
+                    reinterpret_cast<__bf16*>(blk)[e] = zh;
+                    reinterpret_cast<__bf16*>(blk + 1024)[e] = zl;
+                }
+            }
+        }
+        __syncthreads();
+        GDN_PHASE(3);
+
+        // ---- (5) dense part for this wavefront's columns
+        bf16x8 s0h[CT][KS], s0l[CT][KS];
+#pragma unroll
+        for (int st = 0; st < CT; ++st)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const float4 x0 = s0r[st][2 * ks], x1 = s0r[st][2 * ks + 1];
+                const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                split8(x, s0h[st][ks], s0l[st][ks]);
+            }
+        // K S0^T of tile S for the wavefront's column tiles
+        auto ks0 = [&](int S, f32x4 (&out)[CT]) {
+            f32x4 ah[CT], al[CT];
+#pragma unroll
+            for (int st = 0; st < CT; ++st) ah[st] = al[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 ka = k_frag(16 * S + lc, ks);
+#pragma unroll
+                for (int st = 0; st < CT; ++st) {
+                    ah[st] = mfma(ka, s0h[st][ks], ah[st]);
+                    al[st] = mfma(ka, s0l[st][ks], al[st]);
                 }
             }
 #pragma unroll
-            for (int bb = 0; bb < ZR; ++bb)
-                if (bb < m) zc[o + bb] = z[bb] * bet[pathc[o + bb]];
-        } else {
-            for (int bb = 0; bb < m; ++bb) zc[o + bb] = yc[o + bb];
-            for (int aa = m - 1; aa >= 1; --aa) {
-                const float za = zc[o + aa];
-                const int oa = ofp[o + aa];
-                for (int bb = 0; bb < aa; ++bb) zc[o + bb] -= za * xc[oa + bb];
+            for (int st = 0; st < CT; ++st) out[st] = ah[st] + al[st];
+        };
+        // gamma o (Q S0^T) of tile I
+        auto qs0 = [&](int I, f32x4 (&out)[CT]) {
+            f32x4 ah[CT], al[CT];
+#pragma unroll
+            for (int st = 0; st < CT; ++st) ah[st] = al[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 qa = q_frag(16 * I + lc, ks);
+#pragma unroll
+                for (int st = 0; st < CT; ++st) {
+                    ah[st] = mfma(qa, s0h[st][ks], ah[st]);
+                    al[st] = mfma(qa, s0l[st][ks], al[st]);
+                }
             }
-            for (int bb = 0; bb < m; ++bb) zc[o + bb] *= bet[pathc[o + bb]];
-        }
-        if (DENSE) {
-            // scatter the row into the A-fragment blocks of the Z~ R' product:
-            // block (I, kap) = rows 16I.., nodes 32kap..; node t sits in lane
-            // group ((t >> 2) & 3), slot 4 ((t >> 4) & 1) + (t & 3)
-            const int I = i >> 4;
-            unsigned char* rowblk = Zd + 2048 * zblocks_before(I);
-            for (int bb = 0; bb < m; ++bb) {
-                const int t = pathc[o + bb];
-                const float zz = zc[o + bb];
-                const __bf16 zh = static_cast<__bf16>(zz);
-                const __bf16 zl = static_cast<__bf16>(zz - static_cast<float>(zh));
-                const int ln = (((t >> 2) & 3) << 4) | (i & 15);
-                const int e = ln * 8 + (((t >> 4) & 1) << 2) + (t & 3);
-                unsigned char* blk = rowblk + 2048 * (t >> 5);
-                reinterpret_cast<__bf16*>(blk)[e] = zh;
-                reinterpret_cast<__bf16*>(blk + 1024)[e] = zl;
+#pragma unroll
+            for (int st = 0; st < CT; ++st)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) out[st][rr] = (ah[st][rr] + al[st][rr]) * gam[16 * I + 4 * lg + rr];
+        };
+
+        // For DENSE every tile's K S0^T and Q S0^T are taken now, which frees
+        // the staged K/Q: the next item's K/Q are prefetched into registers
+        // here and written to LDS at the end of this item.
+        constexpr int PT = DENSE ? NTMAX : 1;
+        f32x4 pk[PT][CT], pq[PT][CT];
+        if constexpr (DENSE) {
+#pragma unroll
+            for (int S = 0; S < NTMAX; ++S) {
+                if (S < NT) {
+                    ks0(S, pk[S]);
+                    qs0(S, pq[S]);
+                } else {
+#pragma unroll
+                    for (int st = 0; st < CT; ++st) pk[S][st] = pq[S][st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
             }
         }
-    }
-    __syncthreads();
+        GDN_PHASE(4);
+        if (next_new_kh) prefetch_kq(nit, tid, N);
 
-    // ---- (5) dense part for this wavefront's 16 value columns
-    bf16x8 s0h[KS], s0l[KS];
+        // R' = V - gamma o (K S0^T) as B fragments of the Z~ R' product:
+        // k-step kap covers nodes [32 kap, 32 kap + 32); lane (lc, lg) holds
+        // rows 32 kap + 16 half + 4 lg + rr in slot 4 half + rr.
+        bf16x8 rh[CT][NKMAX], rl[CT][NKMAX];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const float4 x0 = s0r[2 * ks], x1 = s0r[2 * ks + 1];
-        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        split8(x, s0h[ks], s0l[ks]);
-    }
-
-    // R' = V - gamma o (K S0^T) as B fragments of the Z~ R' product: k-step
-    // kap covers nodes [32 kap, 32 kap + 32); lane (lc, lg) holds rows
-    // 32 kap + 16 half + 4 lg + rr in slot 4 half + rr.
-    bf16x8 rh[NKMAX], rl[NKMAX];
+        for (int kap = 0; kap < NKMAX; ++kap) {
+            float rt[CT][8];
 #pragma unroll
-    for (int kap = 0; kap < NKMAX; ++kap) {
-        float rt[8];
+            for (int half = 0; half < 2; ++half) {
+                const int S = 2 * kap + half;
+                f32x4 pks[CT];
+                if constexpr (DENSE) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int S = 2 * kap + half;
-            if (S < NT) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    for (int st = 0; st < CT; ++st) pks[st] = pk[S][st];
+                } else {
+                    if (S < NT) {
+                        ks0(S, pks);
+                    } else {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 ka = k_frag(16 * S + lc, ks);
-                    acc = mfma(ka, s0h[ks], acc);
-                    acc = mfma(ka, s0l[ks], acc);
+                        for (int st = 0; st < CT; ++st) pks[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
                 }
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int srow = 16 * S + 4 * lg + rr;
-                    const float vv = srow < N ? to_f32(vraw[S][rr]) : 0.f;
-                    rt[4 * half + rr] = vv - gam[srow] * acc[rr];
+                    const uint32_t w = srow < N ? vraw[S][rr] : 0u;
+                    const float gm = gam[srow];
+#pragma unroll
+                    for (int st = 0; st < CT; ++st) {
+                        const float vv = __uint_as_float(st == 0 ? w << 16 : w & 0xFFFF0000u);
+                        rt[st][4 * half + rr] = vv - gm * pks[st][rr];
+                    }
                 }
-            } else {
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) rt[4 * half + rr] = 0.f;
             }
+#pragma unroll
+            for (int st = 0; st < CT; ++st) split8(rt[st], rh[st][kap], rl[st][kap]);
         }
-        split8(rt, rh[kap], rl[kap]);
-    }
 
-    // O tiles: gamma o (Q S0^T) + Z~ R'
-    for (int I = 0; I < NT; ++I) {
-        const int irow = 16 * I + lc;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        GDN_PHASE(5);
+        // O tiles: gamma o (Q S0^T) + Z~ R'
+        const size_t obase = static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV + column(0);
+        auto store_tile = [&](int I, const f32x4 (&acc)[CT]) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 qa = q_frag(irow, ks);
-            acc = mfma(qa, s0h[ks], acc);
-            acc = mfma(qa, s0l[ks], acc);
-        }
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = 16 * I + 4 * lg + rr;
+                if (i < N) {
+                    float* orow = a.o + obase + static_cast<size_t>(i) * Hv * DV;
+                    if (CT == 1)
+                        *orow = acc[0][rr];
+                    else
+                        *reinterpret_cast<float2*>(orow) = make_float2(acc[0][rr], acc[CT - 1][rr]);
+                }
+            }
+        };
+        if constexpr (DENSE) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) acc[rr] *= gam[16 * I + 4 * lg + rr];
-        if (DENSE) {
-            const unsigned char* rowblk = Zd + 2048 * zblocks_before(I) + 16 * lane;
+            for (int I = 0; I < NTMAX; ++I) {
+                if (I < NT) {
+                    f32x4 acc[CT];
 #pragma unroll
-            for (int kap = 0; kap < NKMAX; ++kap) {
-                if (2 * kap <= I) {
-                    const bf16x8 zh = load_frag(rowblk + 2048 * kap);
-                    const bf16x8 zl = load_frag(rowblk + 2048 * kap + 1024);
-                    acc = mfma(zh, rh[kap], acc);
-                    acc = mfma(zh, rl[kap], acc);
-                    acc = mfma(zl, rh[kap], acc);
+                    for (int st = 0; st < CT; ++st) acc[st] = pq[I][st];
+                    const unsigned char* blk = Zd + 2048 * zblocks_before(I) + 16 * lane;
+#pragma unroll
+                    for (int kap = 0; kap <= I / 2; ++kap) {
+                        const bf16x8 zh = load_frag(blk + 2048 * kap);
+                        const bf16x8 zl = load_frag(blk + 2048 * kap + 1024);
+#pragma unroll
+                        for (int st = 0; st < CT; ++st) {
+                            acc[st] = mfma(zh, rh[st][kap], acc[st]);
+                            acc[st] = mfma(zh, rl[st][kap], acc[st]);
+                            acc[st] = mfma(zl, rh[st][kap], acc[st]);
+                        }
+                    }
+                    store_tile(I, acc);
                 }
             }
         } else {
-            // this lane's row of Z~, scanned once in node order
-            int p = 0, pend = 0;
-            if (irow < N) {
-                p = off[irow];
-                pend = p + dep[irow];
-            }
-#pragma unroll
-            for (int kap = 0; kap < NKMAX; ++kap) {
-                if (2 * kap > I) continue;
-                float f[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) f[j] = 0.f;
-                while (p < pend) {
-                    const int t = pathc[p];
-                    if (t >= 32 * kap + 32) break;
-                    const int dt = t - 32 * kap;
-                    if (((dt >> 2) & 3) == lg) {
-                        const int slot = ((dt >> 4) << 2) | (dt & 3);
-                        const float z = zc[p];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) f[j] = slot == j ? z : f[j];
-                    }
-                    ++p;
+            for (int I = 0; I < NT; ++I) {
+                const int irow = 16 * I + lc;
+                f32x4 acc[CT];
+                qs0(I, acc);
+                // this lane's row of Z~, scanned once in node order
+                int p = 0, pend = 0;
+                if (irow < N) {
+                    p = off[irow];
+                    pend = p + dep[irow];
                 }
-                bf16x8 zh, zl;
-                split8(f, zh, zl);
-                acc = mfma(zh, rh[kap], acc);
-                acc = mfma(zh, rl[kap], acc);
-                acc = mfma(zl, rh[kap], acc);
+#pragma unroll
+                for (int kap = 0; kap < NKMAX; ++kap) {
+                    if (2 * kap > I) continue;
+                    float f[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) f[j] = 0.f;
+                    while (p < pend) {
+                        const int t = pathc[p];
+                        if (t >= 32 * kap + 32) break;
+                        const int dt = t - 32 * kap;
+                        if (((dt >> 2) & 3) == lg) {
+                            const int slot = ((dt >> 4) << 2) | (dt & 3);
+                            const float z = yc[p];
+#pragma unroll
+                            for (int j = 0; j < 8; ++j) f[j] = slot == j ? z : f[j];
+                        }
+                        ++p;
+                    }
+                    bf16x8 zh, zl;
+                    split8(f, zh, zl);
+#pragma unroll
+                    for (int st = 0; st < CT; ++st) {
+                        acc[st] = mfma(zh, rh[st][kap], acc[st]);
+                        acc[st] = mfma(zh, rl[st][kap], acc[st]);
+                        acc[st] = mfma(zl, rh[st][kap], acc[st]);
+                    }
+                }
+                store_tile(I, acc);
             }
         }
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int i = 16 * I + 4 * lg + rr;
-            if (i < N) a.o[(static_cast<size_t>(b) * N + i) * Hv * DV + static_cast<size_t>(h) * DV + col] = acc[rr];
+        GDN_PHASE(6);
+        cur_b = b;
+        cur_kh = kh;
+        // DENSE: the staged K/Q are no longer read; put the next item's there
+        kq_staged = DENSE && next_new_kh;
+        if (kq_staged) {
+            __syncthreads();
+            stage_kq();
         }
+        __syncthreads();  // the next item rewrites LDS
+        GDN_PHASE(7);
     }
+}
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <int NMAX, int DK, int DV>
 hipError_t verify_fast(const VerifyArgs& a, hipStream_t stream) {
-    const int R = a.H_v / a.H_k;
-    const int groups = a.B * a.H_k;
-    const dim3 grid(static_cast<unsigned>(8 * R) * static_cast<unsigned>((groups + 7) / 8));
-    hipLaunchKernelGGL((verify_fast_kernel<NMAX, DK, DV>), grid, dim3(64 * (DV / 16)), 0, stream, a);
+    const int items = a.B * a.H_v;
+    const int wgs = min(items, device_cus());
+    const int per = (items + wgs - 1) / wgs;
+    const dim3 grid(static_cast<unsigned>((items + per - 1) / per));
+    hipLaunchKernelGGL((verify_fast_kernel<NMAX, DK, DV>), grid, dim3(256), 0, stream, a, per);
     return hipGetLastError();
 }
 
