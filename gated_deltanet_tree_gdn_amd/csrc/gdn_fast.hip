@@ -43,6 +43,7 @@
 #include <cstdint>
 
 #include "gdn_internal.h"
+#include "gdn_mfma.h"
 #include "gdn_walk.h"
 
 // Phase markers: no-ops here; a profiling build defines them to accumulate
@@ -54,25 +55,6 @@
 
 namespace gdn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// x ~= hi + lo with hi = bf16(x) (nearest) and lo = bf16(x - hi).
-__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const __bf16 h = static_cast<__bf16>(x[j]);
-        hi[j] = h;
-        lo[j] = static_cast<__bf16>(x[j] - static_cast<float>(h));
-    }
-}
-
-__device__ __forceinline__ bf16x8 load_frag(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 __device__ __forceinline__ uint4 mask4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
 

@@ -43,13 +43,16 @@ struct CommitArgs {
     const int32_t* accepted;
     float* S_new;
     int32_t* accept_status;  // [B]: 0 or GDN_ERR_ACCEPT
+    int force_walk;          // 1: per-node path walk even for bf16 (GDN_FORCE_SIMPLE=1)
 };
 
 // Verify dispatch: the MFMA path for bf16 q/k/v, the per-node walk otherwise.
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // The per-node walk for every batch element (any dtype).
 hipError_t launch_verify_simple(const VerifyArgs& a, hipStream_t stream);
+// Commit dispatch: the MFMA chunked path for bf16 k/v, the per-node walk otherwise.
 hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
+hipError_t launch_commit_simple(const CommitArgs& a, hipStream_t stream);
 hipError_t launch_ancestors(int B, int N, const int32_t* parent, uint32_t* anc, int32_t* depth,
                             int32_t* tree_status, hipStream_t stream);
 

@@ -221,7 +221,7 @@ hipError_t launch_verify_simple(const VerifyArgs& a, hipStream_t stream) {
     return a.d_k == 64 ? verify_simple<float, 64>(a, stream) : verify_simple<float, 128>(a, stream);
 }
 
-hipError_t launch_commit(const CommitArgs& a, hipStream_t stream) {
+hipError_t launch_commit_simple(const CommitArgs& a, hipStream_t stream) {
     if (a.qkv_dtype == GDN_BF16)
         return a.d_k == 64 ? commit_simple<uint16_t, 64>(a, stream) : commit_simple<uint16_t, 128>(a, stream);
     return a.d_k == 64 ? commit_simple<float, 64>(a, stream) : commit_simple<float, 128>(a, stream);

@@ -192,7 +192,7 @@ gdn_status gdn_commit_path(gdn_ctx* ctx, const int32_t* accepted, float* S_new, 
     }
     if (ctx->validate) GDN_TRY(host_check_accepted(d, accepted, stream));
     gdn::CommitArgs a{d.B, d.N, d.H_k, d.H_v, d.d_k, d.d_v, d.qkv_dtype, ctx->k, ctx->v, ctx->g, ctx->beta,
-                      ctx->parent, ctx->S0, accepted, S_new, ctx->status + d.B};
+                      ctx->parent, ctx->S0, accepted, S_new, ctx->status + d.B, ctx->force_walk ? 1 : 0};
     hipError_t e = gdn::launch_commit(a, stream);
     if (e != hipSuccess) return hip_fail(e, "commit launch");
     ctx->have_commit = true;

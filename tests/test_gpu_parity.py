@@ -334,3 +334,22 @@ def test_walk_kernels_parity(name, monkeypatch):
     o, ctx = run_verify(d)
     gdn.gdn_ctx_status(ctx)
     assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), f"walk {name} o")
+    acc = np.random.default_rng(5).integers(-1, cfg.N, size=cfg.B).astype(np.int32)
+    S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
+    gdn.gdn_ctx_status(ctx)
+    assert_close(S_new.cpu().numpy(), oracle.commit_inputs(inp, accepted=acc), f"walk {name} S_new")
+
+
+@pytest.mark.parametrize("tree", ["chain", "best_first"])
+def test_commit_every_path_length(tree):
+    """commit at every node of one tree: path lengths 1 .. depth, across the
+    16-node chunk boundaries of the chunked path update"""
+    cfg = G.shrink(G.CONFIGS["bestfirst128"], B=1, H_k=2, H_v=4, N=50, tree=tree, max_depth=50)
+    inp = G.make_inputs(cfg, seed=6)
+    d = G.to_device(inp)
+    say(f"[commit] every node of a {tree} tree")
+    _, ctx = run_verify(d)
+    for a in range(-1, cfg.N):
+        acc = np.array([a], np.int32)
+        S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
+        assert_close(S_new.cpu().numpy(), oracle.commit_inputs(inp, accepted=acc), f"commit at {a}")
