@@ -33,7 +33,8 @@ if ROOT not in sys.path:
 METRIC = "GDN tree-verify nodes·heads/s per layer at B=32,N=128; % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "bestfirst_b32n128"
-KERNEL_SOURCES = ["gdn_tree_api.cpp", "gdn_simple.hip"]
+KERNEL_SOURCES = ["gdn_tree_api.cpp", "gdn_internal.h", "gdn_mfma.h", "gdn_walk.h", "gdn_simple.hip",
+                  "gdn_fast.hip", "gdn_commit.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_verify_bestfirst_b32n128.json")
 
 
@@ -64,9 +65,10 @@ def commit_bytes(cfg, path_len) -> int:
     return (2 * B * Hv * dv * dk * 4 + rows * (Hk * dk * e + Hv * (dv * e + 8)) + B * N * 4 + B * 4)
 
 
-def read_traffic(per_launch_bytes):
-    """HBM traffic of one verify launch from committed rocprofv3 counters,
-    if they were taken on the current kernel sources; else None."""
+def read_traffic(kernel):
+    """HBM bytes of one launch of `kernel` ("verify" or "commit") from the
+    committed rocprofv3 counters, if they were taken on the current kernel
+    sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -74,26 +76,73 @@ def read_traffic(per_launch_bytes):
         return None
     if t.get("kernel_source_sha") != kernel_source_sha():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get(kernel, {}).get("hbm_bytes_per_launch")
+
+
+COPY_CALLS = 5
+KERNELS = {"verify": "verify_fast_kernel", "commit": "commit_mfma_kernel", "copy": "MulFunctor"}
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each kernel, scaled by
+    the factor that maps the same counter to the known bytes of the
+    calibration copy, written to TRAFFIC_FILE with the kernel sources' hash."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {k: [] for k in KERNELS}
+        with open(path) as f:
+            rows = sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            for k, pat in KERNELS.items():
+                if pat in r["Kernel_Name"]:
+                    vals[k].append(float(r["Counter_Value"]))
+        vals["copy"] = vals["copy"][-COPY_CALLS:]
+        return {k: (sum(v) / len(v) if v else None) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+    fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, nw = per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = float(copy_mib << 10)
+    ff, fw = copy_kib / fetch["copy"], copy_kib / write["copy"]
+    out = {"kernel_source_sha": kernel_source_sha(), "copy_kib": copy_kib,
+           "fetch_factor": ff, "write_factor": fw, "dispatches": {"fetch": nf, "write": nw}}
+    for k in ("verify", "commit"):
+        if fetch[k] is None or write[k] is None:
+            continue
+        out[k] = {"fetch_kib": fetch[k], "write_kib": write[k],
+                  "hbm_bytes_per_launch": 1024.0 * (fetch[k] * ff + write[k] * fw)}
+    out["hbm_bytes_per_launch"] = out.get("verify", {}).get("hbm_bytes_per_launch")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(sets0, cfg, max_seqs):
-    """The fp64 oracle (memoised form, as it stands) on a bounded sample of
-    the same inputs: the first `max_seqs` sequences of input set 0."""
+    """The fp64 oracle, as it stands (the plain per-path replay), on a
+    bounded sample of the same workload: verify and commit of the first
+    `max_seqs` sequences of input set 0."""
     import numpy as np
     import oracle
 
     nb = min(max_seqs, cfg.B)
     host = {n: sets0[n][:nb].float().cpu().numpy().astype(np.float64) for n in ("q", "k", "v", "g", "beta", "S0")}
     host["parent"] = sets0["parent"][:nb].cpu().numpy()
+    acc = sets0["accepted"][:nb].cpu().numpy()
     threads = min(os.cpu_count() or 1, 16)
-    t0 = time.perf_counter()
-    oracle.verify_inputs(host, memo=True, threads=threads)
+    # repeat the sample until about a second of wall time (10-20 s of CPU work)
+    reps, t0 = 0, time.perf_counter()
+    while reps < 50 and (reps == 0 or time.perf_counter() - t0 < 1.0):
+        oracle.verify_inputs(host, threads=threads)
+        oracle.commit_inputs(host, accepted=acc, threads=threads)
+        reps += 1
     dt = time.perf_counter() - t0
-    return {"value": nb * cfg.N * cfg.H_v / dt, "unit": "nodes·heads/s", "cores": threads,
+    return {"value": reps * nb * cfg.N * cfg.H_v / dt, "unit": "nodes·heads/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"fp64 memoised oracle, verify of sequences 0..{nb - 1} of input set 0 "
-                      f"({nb}x{cfg.N} nodes x {cfg.H_v} heads), {dt:.2f} s wall"}
+            "sample": f"fp64 oracle (per-path replay), verify + commit of sequences 0..{nb - 1} of input "
+                      f"set 0 ({nb}x{cfg.N} nodes x {cfg.H_v} heads), {reps} repetitions on {threads} "
+                      f"threads, {dt:.2f} s wall"}
 
 
 def main():
@@ -105,8 +154,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the CPU-oracle sample (0: skip)")
     ap.add_argument("--kernel-only", action="store_true",
-                    help="only run verify back-to-back (for profiler runs); prints progress, no JSON")
+                    help="profiler runs: verify + commit back to back, then the calibration copies; "
+                         "prints progress, no JSON")
+    ap.add_argument("--copy-mib", type=int, default=256, help="size of each calibration copy (--kernel-only)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter CSVs of a --kernel-only run into the "
+                         "per-launch HBM traffic file read by this script")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, copy_mib=args.copy_mib)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; --gpus must be 1 "
@@ -162,11 +220,19 @@ def main():
         gdn.gdn_commit_path(s["ctx"], s["accepted"], S_new=s["S_new"], stream=stream)
 
     if args.kernel_only:
-        for i in range(args.warmup + args.steps):
-            verify(sets[i % len(sets)])
-            if i % 50 == 0:
-                torch.cuda.synchronize()
-                print(f"kernel-only: {i} verify calls", flush=True)
+        # each kernel back to back, as the per-kernel event timing below runs it
+        for name, fn in (("verify", verify), ("commit", commit)):
+            for i in range(args.warmup + args.steps):
+                fn(sets[i % len(sets)])
+                if i % 50 == 0:
+                    torch.cuda.synchronize()
+                    print(f"kernel-only: {i} {name} calls", flush=True)
+            torch.cuda.synchronize()
+        # calibration: a plain streaming kernel of known size (read n, write n bytes)
+        src = torch.ones(args.copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(COPY_CALLS):
+            torch.mul(src, 2.0, out=dst)
         torch.cuda.synchronize()
         print("kernel-only: done", flush=True)
         return
@@ -213,7 +279,7 @@ def main():
     vbytes = verify_bytes(cfg)
     cbytes = float(np.mean([commit_bytes(cfg, pl) for pl in path_lens]))
     achieved = vbytes / (verify_ms * 1e-3) / 1e9
-    traffic = read_traffic(vbytes)
+    traffic = read_traffic("verify")
     out = {
         "metric": METRIC,
         "value": nh / (step_ms * 1e-3),
@@ -225,17 +291,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic (seeded best-first trees and N(0,1)-derived tensors; no model weights)",
         "config": {"workload": WORKLOAD, "B": cfg.B, "N": cfg.N, "H_k": cfg.H_k, "H_v": cfg.H_v,
                    "d_k": cfg.d_k, "d_v": cfg.d_v, "qkv": cfg.dtype, "state": "f32", "output": "f32",
                    "tree": f"best_first depth<={cfg.max_depth}",
                    "mean_strict_ancestors": float(np.mean([a["mean_strict_ancestors"] for a in anc_depth])),
                    "max_depth": int(max(a["max_depth"] for a in anc_depth)),
-                   "rotating_sets": len(sets), "step": "gdn_tree_verify + gdn_commit_path"},
+                   "rotating_sets": len(sets), "step": "gdn_tree_verify + gdn_commit_path",
+                   "arithmetic": "bf16 MFMA with fp32 accumulation; fp32 operands as bf16 hi+lo pairs; "
+                                 "fp32 VALU for gates and the triangular solves"},
         "verify": {"ms": verify_ms, "nodes_heads_per_s": nh / (verify_ms * 1e-3),
                    "algorithmic_bytes": vbytes, "GBps": achieved},
-        "commit": {"ms": commit_ms, "algorithmic_bytes": cbytes, "GBps": cbytes / (commit_ms * 1e-3) / 1e9},
+        "commit": {"ms": commit_ms, "algorithmic_bytes": cbytes, "GBps": cbytes / (commit_ms * 1e-3) / 1e9,
+                   "frac": cbytes / (commit_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": read_traffic("commit")},
         "roofline": {"bound": "hbm", "kernel": "gdn_tree_verify", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic},
