@@ -51,6 +51,7 @@
 #ifndef GDN_PHASE
 #define GDN_PHASE_INIT
 #define GDN_PHASE(k)
+#define GDN_PHASE_END
 #endif
 
 namespace gdn {
@@ -744,7 +745,22 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
         __syncthreads();  // the next item rewrites LDS
         GDN_PHASE(7);
     }
+    GDN_PHASE_END;
 }
+
+
+template <int NMAX, int DK, int DV>
+hipError_t verify_fast(const VerifyArgs& a, hipStream_t stream) {
+    const int items = a.B * a.H_v;
+    const int wgs = min(items, device_cus());
+    const int per = (items + wgs - 1) / wgs;
+    const dim3 grid(static_cast<unsigned>((items + per - 1) / per));
+    hipLaunchKernelGGL((verify_fast_kernel<NMAX, DK, DV>), grid, dim3(256), 0, stream, a, per);
+    return hipGetLastError();
+}
+
+
+}  // namespace
 
 int device_cus() {
     static int cached[64] = {0};
@@ -758,29 +774,12 @@ int device_cus() {
     return cached[dev];
 }
 
-template <int NMAX, int DK, int DV>
-hipError_t verify_fast(const VerifyArgs& a, hipStream_t stream) {
-    const int items = a.B * a.H_v;
-    const int wgs = min(items, device_cus());
-    const int per = (items + wgs - 1) / wgs;
-    const dim3 grid(static_cast<unsigned>((items + per - 1) / per));
-    hipLaunchKernelGGL((verify_fast_kernel<NMAX, DK, DV>), grid, dim3(256), 0, stream, a, per);
-    return hipGetLastError();
-}
-
-template <int DK, int DV>
-hipError_t verify_fast_n(const VerifyArgs& a, hipStream_t stream) {
-    if (a.N <= 64) return verify_fast<64, DK, DV>(a, stream);
-    if (a.N <= 128) return verify_fast<128, DK, DV>(a, stream);
-    return verify_fast<256, DK, DV>(a, stream);
-}
-
-}  // namespace
-
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     if (a.qkv_dtype != GDN_BF16 || a.force_walk) return launch_verify_simple(a, stream);
-    if (a.d_k == 128) return a.d_v == 128 ? verify_fast_n<128, 128>(a, stream) : verify_fast_n<128, 64>(a, stream);
-    return a.d_v == 128 ? verify_fast_n<64, 128>(a, stream) : verify_fast_n<64, 64>(a, stream);
+    // trees of up to 128 nodes: two workgroups per compute unit
+    if (a.N <= 128) return launch_verify_grp(a, stream);
+    if (a.d_k == 128) return a.d_v == 128 ? verify_fast<256, 128, 128>(a, stream) : verify_fast<256, 128, 64>(a, stream);
+    return a.d_v == 128 ? verify_fast<256, 64, 128>(a, stream) : verify_fast<256, 64, 64>(a, stream);
 }
 
 }  // namespace gdn

@@ -48,6 +48,10 @@ struct CommitArgs {
 
 // Verify dispatch: the MFMA path for bf16 q/k/v, the per-node walk otherwise.
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
+// The MFMA verify for bf16 and N <= 128, two workgroups per compute unit.
+hipError_t launch_verify_grp(const VerifyArgs& a, hipStream_t stream);
+// Compute units of the current device (cached per device).
+int device_cus();
 // The per-node walk for every batch element (any dtype).
 hipError_t launch_verify_simple(const VerifyArgs& a, hipStream_t stream);
 // Commit dispatch: the MFMA chunked path for bf16 k/v, the per-node walk otherwise.

@@ -22,6 +22,13 @@ __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f3
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x16_bf16: the same layout with 4 k-slots per lane,
+// 4 (l / 16) .. 4 (l / 16) + 3 (bf16 bits in shorts).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(const s16x4& a, const s16x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 // x ~= hi + lo with hi = bf16(x) (nearest) and lo = bf16(x - hi), so a
 // product with an exact bf16 operand keeps about 16 significant bits.
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
