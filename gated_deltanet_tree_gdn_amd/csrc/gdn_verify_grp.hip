@@ -38,9 +38,13 @@
 #include "gdn_mfma.h"
 #include "gdn_walk.h"
 
+// Phase boundaries.  In the product build they are scheduling fences only
+// (no instruction): code is not moved across them, which keeps each
+// phase's registers to itself.  A profiling build defines them to
+// accumulate per-phase cycle counts.
 #ifndef GDN_PHASE
 #define GDN_PHASE_INIT
-#define GDN_PHASE(k)
+#define GDN_PHASE(k) (void)__builtin_amdgcn_s_memtime()
 #define GDN_PHASE_END
 #endif
 
@@ -461,21 +465,43 @@ __global__ __launch_bounds__(512) void verify_grp_kernel(VerifyArgs a, int items
                     }
                 }
             }
+            // scatter: every LDS read of a tile issued up front, stores
+            // predicated on the ancestor bit
 #pragma unroll
             for (int j = 0; j < TPW; ++j) {
+                __builtin_amdgcn_sched_barrier(0);
                 if (tcode[j] < 0) continue;
                 const int I = tcode[j] >> 4, J = tcode[j] & 15;
                 const int s = 16 * J + lc;
                 const int ds = dep[s];
+                float gsv[GH], giv[GH][4], biv[GH][4];
+                uint32_t aw[4];
+                int oi[4];
+#pragma unroll
+                for (int e = 0; e < GH; ++e) gsv[e] = Gs[e * NMAX + s];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int i = 16 * I + 4 * lg + rr;
-                    if (i < N && ((anc[i * L::AW + (s >> 5)] >> (s & 31)) & 1u)) {
-                        const int p = off[i] + ds - 1;
-                        for (int e = 0; e < nh; ++e) {
-                            const float D = __expf(Gs[e * NMAX + i] - Gs[e * NMAX + s]);
-                            xc[e * L::XSTR + p] = bet[e * NMAX + i] * D * akk[j][rr];
-                            yc[e * L::CAP + p] = D * aqk[j][rr];
+                    aw[rr] = anc[i * L::AW + (s >> 5)];
+                    oi[rr] = off[i];
+#pragma unroll
+                    for (int e = 0; e < GH; ++e) {
+                        giv[e][rr] = Gs[e * NMAX + i];
+                        biv[e][rr] = bet[e * NMAX + i];
+                    }
+                }
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int i = 16 * I + 4 * lg + rr;
+                    if (i < N && ((aw[rr] >> (s & 31)) & 1u)) {
+                        const int p = oi[rr] + ds - 1;
+#pragma unroll
+                        for (int e = 0; e < GH; ++e) {
+                            if (e < nh) {
+                                const float D = __expf(giv[e][rr] - gsv[e]);
+                                xc[e * L::XSTR + p] = biv[e][rr] * D * akk[j][rr];
+                                yc[e * L::CAP + p] = D * aqk[j][rr];
+                            }
                         }
                     }
                 }
@@ -541,7 +567,6 @@ __global__ __launch_bounds__(512) void verify_grp_kernel(VerifyArgs a, int items
         GDN_PHASE(4);
 
         // ---- dense part, one head at a time
-        const int NT = (N + 15) >> 4;
         for (int e = 0; e < nh; ++e) {
             // Opaque copies again: addresses below are recomputed per head
             // rather than hoisted out of this loop.
@@ -593,11 +618,11 @@ __global__ __launch_bounds__(512) void verify_grp_kernel(VerifyArgs a, int items
                 GDN_PHASE(11);
 
                 // P = M S0^T of row tile S for M = K or Q, this wavefront's columns
-                auto ms0 = [&](const unsigned char* base, int S) -> f32x4 {
+                auto ms0 = [&](const unsigned char* base, int S, int lcx, int lgx) -> f32x4 {
                     f32x4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
-                        const bf16x8 fa = frag(base, 16 * S + lc, lg, ks);
+                        const bf16x8 fa = frag(base, 16 * S + lcx, lgx, ks);
                         ah = mfma(fa, s0h[ks], ah);
                         al = mfma(fa, s0l[ks], al);
                     }
@@ -612,6 +637,7 @@ __global__ __launch_bounds__(512) void verify_grp_kernel(VerifyArgs a, int items
                 s16x4 eye;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) eye[j] = 4 * lg + j == lc ? static_cast<short>(0x3F80) : short(0);
+                const int NT = (N + 15) >> 4;
                 bf16x8 rh[NKMAX], rl[NKMAX];
 #pragma unroll
                 for (int kap = 0; kap < NKMAX; ++kap) {
@@ -619,12 +645,21 @@ __global__ __launch_bounds__(512) void verify_grp_kernel(VerifyArgs a, int items
 #pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         const int S = 2 * kap + half;
-                        const f32x4 pk = S < NT ? ms0(Ks, S) : f32x4{0.f, 0.f, 0.f, 0.f};
-                        const f32x4 vt = mfma16(__builtin_bit_cast(s16x4, vc[S]), eye, f32x4{0.f, 0.f, 0.f, 0.f});
+                        if (S < NT) {
+                            // gamma is 0 past N; V of the clamped rows is
+                            // masked by a select (no branch around the LDS read)
+                            const f32x4 pk = ms0(Ks, S, lc, lg);
+                            const f32x4 vt = mfma16(__builtin_bit_cast(s16x4, vc[S]), eye, f32x4{0.f, 0.f, 0.f, 0.f});
+                            const f32x4 gm = *reinterpret_cast<const f32x4*>(ge + 16 * S + 4 * lg);
 #pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) {
-                            const int srow = 16 * S + 4 * lg + rr;
-                            rt[4 * half + rr] = srow < N ? vt[rr] - ge[srow] * pk[rr] : 0.f;
+                            for (int rr = 0; rr < 4; ++rr) {
+                                const int srow = 16 * S + 4 * lg + rr;
+                                const float vv = srow < N ? vt[rr] : 0.f;
+                                rt[4 * half + rr] = vv - gm[rr] * pk[rr];
+                            }
+                        } else {
+#pragma unroll
+                            for (int rr = 0; rr < 4; ++rr) rt[4 * half + rr] = 0.f;
                         }
                     }
                     split8(rt, rh[kap], rl[kap]);
