@@ -34,7 +34,7 @@ METRIC = "GDN tree-verify nodes·heads/s per layer at B=32,N=128; % HBM/MFMA roo
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "bestfirst_b32n128"
 KERNEL_SOURCES = ["gdn_tree_api.cpp", "gdn_internal.h", "gdn_mfma.h", "gdn_walk.h", "gdn_simple.hip",
-                  "gdn_fast.hip", "gdn_commit.hip"]
+                  "gdn_fast.hip", "gdn_verify_grp.hip", "gdn_verify_ws.hip", "gdn_commit.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_verify_bestfirst_b32n128.json")
 
 
@@ -80,7 +80,7 @@ def read_traffic(kernel):
 
 
 COPY_CALLS = 5
-KERNELS = {"verify": "verify_fast_kernel", "commit": "commit_mfma_kernel", "copy": "MulFunctor"}
+KERNELS = {"verify": "verify_ws_kernel", "commit": "commit_mfma_kernel", "copy": "MulFunctor"}
 
 
 def write_traffic(fetch_csv, write_csv, copy_mib):

@@ -28,6 +28,7 @@ struct VerifyArgs {
     float* o;
     int32_t* tree_status;  // [B]: 0 or GDN_ERR_TREE
     int force_walk;        // 1: per-node walk even for bf16 (GDN_FORCE_SIMPLE=1)
+    int lockstep;          // 1: trees of <= 128 nodes by the lock-step kernel (GDN_VERIFY_LOCKSTEP=1)
 };
 
 // Arguments of one accepted-path commit.
@@ -50,6 +51,7 @@ struct CommitArgs {
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // The MFMA verify for bf16 and N <= 128, two workgroups per compute unit.
 hipError_t launch_verify_grp(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_verify_ws(const VerifyArgs& a, hipStream_t stream);
 // Compute units of the current device (cached per device).
 int device_cus();
 // The per-node walk for every batch element (any dtype).

@@ -38,13 +38,11 @@
 #include "gdn_mfma.h"
 #include "gdn_walk.h"
 
-// Phase boundaries.  In the product build they are scheduling fences only
-// (no instruction): code is not moved across them, which keeps each
-// phase's registers to itself.  A profiling build defines them to
-// accumulate per-phase cycle counts.
+// Phase boundaries: empty in the product build; a profiling build defines
+// them to accumulate per-phase cycle counts.
 #ifndef GDN_PHASE
 #define GDN_PHASE_INIT
-#define GDN_PHASE(k) (void)__builtin_amdgcn_s_memtime()
+#define GDN_PHASE(k)
 #define GDN_PHASE_END
 #endif
 

@@ -45,6 +45,9 @@
  *  - GDN_FORCE_SIMPLE=1 (read when a context is created) routes that
  *    context's verify to the per-node walk kernels instead of the MFMA path
  *    (for A/B comparison; results agree within the stated tolerance).
+ *    GDN_VERIFY_LOCKSTEP=1 (likewise) verifies bf16 trees of up to 128 nodes
+ *    with the lock-step MFMA kernel instead of the one that overlaps the tree
+ *    and dense parts of consecutive heads (same results up to rounding).
  *  - Calls are asynchronous on `stream` (NULL = the default stream) and
  *    complete in stream order.
  */
@@ -144,9 +147,11 @@ gdn_status gdn_tree_ancestors(const gdn_tree_dims* dims, const int32_t* parent, 
                               int32_t* depth, int32_t* tree_status, hipStream_t stream);
 
 /* Synchronises `stream` and reports the device-side verdicts of the last
- * verify (GDN_ERR_TREE if any sequence had an invalid parent array) and,
- * after a commit, of the last commit (GDN_ERR_ACCEPT if any accepted[b]
- * was out of range).  GDN_OK otherwise. */
+ * verify (GDN_ERR_TREE if any sequence had an invalid parent array;
+ * GDN_ERR_HIP if a bounded wait inside a verify kernel timed out, which
+ * means a defect of the kernel, not of the inputs) and, after a commit, of
+ * the last commit (GDN_ERR_ACCEPT if any accepted[b] was out of range).
+ * GDN_OK otherwise. */
 gdn_status gdn_ctx_status(gdn_ctx* ctx, hipStream_t stream);
 
 /* Static English name of a status code. */

@@ -353,3 +353,35 @@ def test_commit_every_path_length(tree):
         acc = np.array([a], np.int32)
         S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
         assert_close(S_new.cpu().numpy(), oracle.commit_inputs(inp, accepted=acc), f"commit at {a}")
+
+
+def _mixed_depth_inputs(cfg, seed, chain_every):
+    """best-first trees with every `chain_every`-th sequence replaced by a
+    chain (whose pair list exceeds what the MFMA kernels keep in LDS for
+    N > 55, so those sequences take the per-node walk inside them)"""
+    inp = G.make_inputs(cfg, seed=seed)
+    par = inp["parent"].copy()
+    for b in range(0, cfg.B, chain_every):
+        par[b] = np.arange(-1, cfg.N - 1, dtype=np.int32)
+    inp["parent"] = par
+    return inp
+
+
+@pytest.mark.parametrize("lockstep", [0, 1])
+@pytest.mark.parametrize("shape", [
+    dict(B=40, N=128, H_k=3, H_v=9),      # 2 heads per workgroup, sequence and key-head changes inside one
+    dict(B=24, N=64, H_k=4, H_v=16),      # N <= 64 layout, 2 heads per workgroup
+    dict(B=33, N=100, H_k=16, H_v=32),    # 5 heads per workgroup, ragged last workgroup
+])
+def test_pipeline_item_boundaries(shape, lockstep, monkeypatch):
+    """several (sequence, head) items per persistent workgroup: sequence,
+    key-head and deep-tree (walk) boundaries between consecutive items"""
+    if lockstep:
+        monkeypatch.setenv("GDN_VERIFY_LOCKSTEP", "1")
+    cfg = G.shrink(G.CONFIGS["bestfirst_b32n128"], **shape)
+    inp = _mixed_depth_inputs(cfg, seed=11, chain_every=7)
+    d = G.to_device(inp)
+    say(f"[pipeline] {shape} lockstep={lockstep}")
+    o, ctx = run_verify(d)
+    gdn.gdn_ctx_status(ctx)
+    assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), f"pipeline {shape} o")
