@@ -50,6 +50,8 @@
 #define GDN_PHASE_INIT
 #define GDN_PHASE(k)
 #define GDN_PHASE_SNAP
+#define GDN_PHASE_ITER(j)
+#define GDN_PHASE_ARRIVE(j)
 #define GDN_PHASE_END
 #endif
 
@@ -74,15 +76,22 @@ struct WsLds {
     static constexpr int ZD = 2 * KQ_BYTES;          // Z~ fragments of the dense item
     static constexpr int ZD_BYTES = 2048 * ws_zblocks(NMAX / 16);
     // hand-over slots (tree side writes slot (j+1)&1, dense side reads j&1)
-    static constexpr int ZOUT = ZD + ZD_BYTES;       // float[2][CAP]: Y, then the rows of Z~
-    static constexpr int GAMD = ZOUT + 2 * 4 * CAP;  // float[2][NMAX]: gamma (0 past N)
-    static constexpr int SPATH = GAMD + 2 * 4 * NMAX;  // uint8[2][CAP]: ancestor of each pair
-    static constexpr int SPNODE = SPATH + 2 * CAP;   // uint8[2][CAP]: node of each pair
+    // hand-over slots s = 0, 1, each: float[CAP] Y, then the rows of Z~;
+    // float[NMAX] gamma (0 past N); uint8[CAP] ancestor and uint8[CAP] node
+    // of each pair
+    static constexpr int SLOT = ws_align(4 * CAP + 4 * NMAX + 2 * CAP, 16);
+    static constexpr int SLOTS = ZD + ZD_BYTES;
+    static constexpr int S_GAM = 4 * CAP;
+    static constexpr int S_PATH = S_GAM + 4 * NMAX;
+    static constexpr int S_NODE = S_PATH + CAP;
+    static constexpr int SPNODE_END = SLOTS + 2 * SLOT;
     // tree side
-    static constexpr int XC = ws_align(SPNODE + 2 * CAP, 16);  // float[CAP + 16]: X (zero pads)
-    static constexpr int KK = XC + 4 * (CAP + 16);   // float[CAP]: k_i . k_s (per key head)
-    static constexpr int QK = KK + 4 * CAP;          // float[CAP]: q_i . k_s
-    static constexpr int OFP = QK + 4 * CAP;         // uint16[CAP]: path offset of the ancestor
+    static constexpr int XC = ws_align(SPNODE_END, 16);  // float[CAP + 16]: X (zero pads)
+    // float[CAP + 4]: k_i . k_s and q_i . k_s per key head (entry CAP takes
+    // the Gram tile entries that are not ancestor pairs)
+    static constexpr int KK = XC + 4 * (CAP + 16);
+    static constexpr int QK = KK + 4 * (CAP + 4);
+    static constexpr int OFP = QK + 4 * (CAP + 4);   // uint16[CAP]: path offset of the ancestor
     static constexpr int PATH = OFP + 2 * CAP;       // uint8[CAP]
     static constexpr int PNODE = PATH + CAP;         // uint8[CAP]
     static constexpr int NODE = ws_align(PNODE + CAP, 16);
@@ -96,12 +105,15 @@ struct WsLds {
     static constexpr int ANC = GG + 4 * NMAX;        // uint32[NMAX][AW]
     static constexpr int TMASK = ANC + 4 * AW * NMAX;
     static constexpr int MISC = TMASK + 4 * (NMAX / 16);  // int[16]
-    // Gram broadcast of one 16-row tile of K (KS fragments x 64 lanes x 16
-    // bytes), double-buffered: buffer 0 overlays X (free until X is built)
+    // Gram broadcast of 16-row tiles of K (KS fragments x 64 lanes x 16
+    // bytes each), four at a time: buffer 0 overlays X (free until X is
+    // built), 1 is its own, 2 and 3 overlay the hand-over slot of the item
+    // being built (free until its Y is written)
     static constexpr int GB_BYTES = 32 * DK;
     static constexpr int GB0 = XC;
     static constexpr int GB1 = MISC + 64;
     static_assert(GB_BYTES <= 4 * (CAP + 16), "Gram buffer 0 must fit in X");
+    static_assert(2 * GB_BYTES <= SLOT, "Gram buffers 2 and 3 must fit in a hand-over slot");
     static constexpr int TOTAL = GB1 + GB_BYTES;
     // misc[]: 0 tree total, 2 dense sync counter, 3 tree sync counter,
     // 4 spin time-outs, 5/6 slot pair totals, 7/8 slot fallback flags,
@@ -113,7 +125,7 @@ struct WsLds {
     static constexpr int FB_G = FB_KQ + 8 * DK;
     static constexpr int FB_PAR = FB_G + 4 * NMAX;
     static constexpr bool HAS_FALLBACK = CAP < NMAX * (NMAX + 1) / 2;
-    static_assert(!HAS_FALLBACK || FB_PAR + 4 * NMAX <= ZOUT, "fallback buffers must fit in the dense area");
+    static_assert(!HAS_FALLBACK || FB_PAR + 4 * NMAX <= SLOTS, "fallback buffers must fit in the dense area");
     static_assert(TOTAL <= 160 * 1024, "LDS of one compute unit");
 };
 
@@ -136,10 +148,10 @@ __device__ __forceinline__ void role_sync(int* ctr, int nwaves, int& count, int*
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int NMAX, int DK, int DV>
-__global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_per_wg) {
+template <int NMAX, int DK, int DV, int NWD>
+__global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a, int items_per_wg) {
     using L = WsLds<NMAX, DK>;
-    constexpr int NWD = 4;               // dense wavefronts, 32 value columns each (d_v 128)
+    // NWD dense wavefronts
     constexpr int NWT = 4;               // tree wavefronts
     constexpr int TTH = 64 * NWT;
     constexpr int CW = DV / NWD;         // value columns per dense wavefront
@@ -150,8 +162,8 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
     constexpr int NKMAX = NMAX / 32;
     constexpr int KCH = (NMAX * CH + TTH - 1) / TTH;  // K/Q chunks staged per tree thread
     constexpr int ZR = 16;
-    constexpr int TPB = 2;               // Gram tiles in flight per tree wavefront
     static_assert(NMAX <= TTH, "one node per tree thread");
+    static_assert(CT >= 1 && CW * NWD == DV, "whole 16-column tiles per dense wavefront");
     constexpr int RT = NTMAX / NWT;      // K/Q row tiles held per tree wavefront
     static_assert(RT >= 1 && RT <= 2 && NTMAX == RT * NWT, "row tiles per tree wavefront");
 
@@ -193,18 +205,17 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
     unsigned char* Ks = smem + L::KS_OFF;
     unsigned char* Qs = smem + L::QS_OFF;
     unsigned char* Zd = smem + L::ZD;
-    float* zout = reinterpret_cast<float*>(smem + L::ZOUT);
-    float* gamd = reinterpret_cast<float*>(smem + L::GAMD);
-    uint8_t* spath = smem + L::SPATH;
-    uint8_t* spnode = smem + L::SPNODE;
+    auto slot_base = [&](int sl) { return smem + L::SLOTS + sl * L::SLOT; };
+    auto zout_s = [&](int sl) { return reinterpret_cast<float*>(slot_base(sl)); };
+    auto gamd_s = [&](int sl) { return reinterpret_cast<float*>(slot_base(sl) + L::S_GAM); };
+    auto spath_s = [&](int sl) { return slot_base(sl) + L::S_PATH; };
+    auto spnode_s = [&](int sl) { return slot_base(sl) + L::S_NODE; };
     float* xc = reinterpret_cast<float*>(smem + L::XC);
     float* kk = reinterpret_cast<float*>(smem + L::KK);
     float* qk = reinterpret_cast<float*>(smem + L::QK);
     uint16_t* ofp = reinterpret_cast<uint16_t*>(smem + L::OFP);
     uint8_t* pathc = smem + L::PATH;
     uint8_t* pnode = smem + L::PNODE;
-    bf16x8* gbuf0 = reinterpret_cast<bf16x8*>(smem + L::GB0);
-    bf16x8* gbuf1 = reinterpret_cast<bf16x8*>(smem + L::GB1);
     int* par = reinterpret_cast<int*>(smem + L::PAR);
     int* dep = reinterpret_cast<int*>(smem + L::DEP);
     int* off = reinterpret_cast<int*>(smem + L::OFF);
@@ -215,6 +226,8 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
     uint32_t* anc = reinterpret_cast<uint32_t*>(smem + L::ANC);
     uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + L::TMASK);
     int* misc = reinterpret_cast<int*>(smem + L::MISC);
+    bf16x8* gbuf0 = reinterpret_cast<bf16x8*>(smem + L::GB0);
+    bf16x8* gbuf1 = reinterpret_cast<bf16x8*>(smem + L::GB1);
 
     auto item_b = [&](int j) { return (it_begin + j) / Hv; };
     auto item_h = [&](int j) { return (it_begin + j) % Hv; };
@@ -250,29 +263,37 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
             }
         }
     };
+    // natural 16-byte chunk c of K/Q row `row` (elements 8c .. 8c + 7) into
+    // LDS: two 4-element halves, for lane groups g0 and g0 + 1; rows past N
+    // are zero
+    auto put_chunk = [&](int row, int c, uint4 kv, uint4 qv) {
+        const uint32_t keep = row < N ? 0xFFFFFFFFu : 0u;
+        const int sw = row & (CH - 1);
+        const int ks = c >> 2, m = c & 3, hh = m >> 1, g0 = (m & 1) << 1;
+        const int rbase = row * (DK * 2) + 8 * hh;
+        const int pos0 = rbase + (((4 * ks + g0) ^ sw) << 4);
+        const int pos1 = rbase + (((4 * ks + g0 + 1) ^ sw) << 4);
+        *reinterpret_cast<uint2*>(Ks + pos0) = make_uint2(kv.x & keep, kv.y & keep);
+        *reinterpret_cast<uint2*>(Ks + pos1) = make_uint2(kv.z & keep, kv.w & keep);
+        *reinterpret_cast<uint2*>(Qs + pos0) = make_uint2(qv.x & keep, qv.y & keep);
+        *reinterpret_cast<uint2*>(Qs + pos1) = make_uint2(qv.z & keep, qv.w & keep);
+    };
+    // (sequence, key head) whose K/Q the registers hold; loaded on demand
+    int kq_b = -1, kq_kh = -1;
+    auto hold_kq = [&](int j) {
+        if (item_b(j) != kq_b || item_kh(j) != kq_kh) {
+            load_kq(j);
+            kq_b = item_b(j);
+            kq_kh = item_kh(j);
+        }
+    };
     auto stage_kq = [&]() {
 #pragma unroll
-        for (int u = 0; u < RT; ++u) {
-            const int row = 16 * tile_of(u) + lc;
-            const uint32_t keep = row < N ? 0xFFFFFFFFu : 0u;
-            const int sw = row & (CH - 1);
+        for (int u = 0; u < RT; ++u)
 #pragma unroll
-            for (int t = 0; t < KS; ++t) {
-                // natural chunk c holds elements 8c .. 8c + 7: two 4-element
-                // halves for lane groups g0 and g0 + 1
-                const int c = KS * lg + t;
-                const int ks = c >> 2, m = c & 3, hh = m >> 1, g0 = (m & 1) << 1;
-                const int rbase = row * (DK * 2) + 8 * hh;
-                const int pos0 = rbase + (((4 * ks + g0) ^ sw) << 4);
-                const int pos1 = rbase + (((4 * ks + g0 + 1) ^ sw) << 4);
-                const uint4 kv = __builtin_bit_cast(uint4, kf[u][t]);
-                const uint4 qv = __builtin_bit_cast(uint4, qf[u][t]);
-                *reinterpret_cast<uint2*>(Ks + pos0) = make_uint2(kv.x & keep, kv.y & keep);
-                *reinterpret_cast<uint2*>(Ks + pos1) = make_uint2(kv.z & keep, kv.w & keep);
-                *reinterpret_cast<uint2*>(Qs + pos0) = make_uint2(qv.x & keep, qv.y & keep);
-                *reinterpret_cast<uint2*>(Qs + pos1) = make_uint2(qv.z & keep, qv.w & keep);
-            }
-        }
+            for (int t = 0; t < KS; ++t)
+                put_chunk(16 * tile_of(u) + lc, KS * lg + t, __builtin_bit_cast(uint4, kf[u][t]),
+                          __builtin_bit_cast(uint4, qf[u][t]));
     };
     // node scalars of the next tree item, loaded ahead
     float g_pf, b_pf;
@@ -284,6 +305,31 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
         g_pf = a.g[nh];
         b_pf = a.beta[nh];
         p_pf = a.parent[static_cast<size_t>(bb) * N + i];
+    };
+
+    // Gram tile (I, J) (lane: rows 16 I + 4 lg + rr, column 16 J + lc) into
+    // the pair list: the value of pair (i, s) lands at path position
+    // dep[s] - 1 of node i
+    auto put_pairs = [&](int I, int J, const f32x4& akk, const f32x4& aqk) {
+        const int sn = 16 * J + lc;
+        const int ds = dep[sn];
+        uint32_t aw[4];
+        int oi[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int i = 16 * I + 4 * lg + rr;
+            aw[rr] = anc[i * L::AW + (sn >> 5)];
+            oi[rr] = off[i];
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int i = 16 * I + 4 * lg + rr;
+            if (i < N && ((aw[rr] >> (sn & 31)) & 1u)) {
+                const int p = oi[rr] + ds - 1;
+                kk[p] = akk[rr];
+                qk[p] = aqk[rr];
+            }
+        }
     };
 
     // tree part of item j into slot j & 1
@@ -305,13 +351,11 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
         }
         if (new_b && ttid < NMAX / 16) tmask[ttid] = 0u;
     };
-    auto tree_item = [&](int j) {
-        const int b = item_b(j), h = item_h(j), kh = item_kh(j);
-        const int slot = j & 1;
-        const bool new_b = b != t_b;
-        const bool new_kh = new_b || kh != t_kh;
+    // a new sequence: depth, path offsets, paths, ancestor bits, tile mask
+    auto tree_struct = [&](int j) {
+        const int b = item_b(j), h = item_h(j);
         GDN_PHASE(5);
-        if (new_b) {
+        {
             tree_sync();
             GDN_PHASE(1);
             // depth: every node walks up to its root (parents precede their
@@ -379,10 +423,14 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
                 for (int w = 0; w < L::AW; ++w) anc[i * L::AW + w] = bits[w];
             }
             tree_sync();
-            tree_sync();
             t_b = b;
             t_kh = -1;
         }
+    };
+    // the item's pair total and walk flag for the dense side; false for an
+    // item the dense side walks
+    auto tree_check = [&](int j) -> bool {
+        const int slot = j & 1;
         const int total = t_total;
         if (ttid == 0) {
             misc[5 + slot] = total;
@@ -390,11 +438,16 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
         }
         if (total > L::CAP) {
             tree_sync();
-            return;   // the dense side walks this item
+            return false;
         }
+        return true;
+    };
+    // G and gamma per node
+    auto tree_g = [&](int j) {
+        const int slot = j & 1;
         GDN_PHASE(8);
-        // g of every node written (the structure build above syncs too)
-        if (!new_b) tree_sync();
+        // g of every node written, the Gram buffers in the slot read
+        tree_sync();
         GDN_PHASE(9);
         // G and gamma per node
         if (ttid < NMAX) {
@@ -413,63 +466,94 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
                 }
             }
             Gs[i] = G;
-            gamd[slot * NMAX + i] = i < N ? __expf(G) : 0.f;
+            gamd_s(slot)[i] = i < N ? __expf(G) : 0.f;
         }
         GDN_PHASE(10);
-        // Gram values k_i . k_s and q_i . k_s of the ancestor pairs, for a new
-        // key head: one round per column tile J, whose K rows its owner
-        // broadcasts through LDS; each wavefront multiplies them with its own
-        // row tiles I >= J that hold pairs.  The value of pair (i, s) lands
-        // at path position dep[s] - 1 of node i.
-        if (new_kh) {
-            const int NT = (N + 15) >> 4;
-            for (int J = 0; J < NT; ++J) {
-                bf16x8* gb = (J & 1) ? gbuf1 : gbuf0;
-                const int owner = J < NWT ? J : NTMAX - 1 - J;
-                if (twave == owner) {
+    };
+    // Gram values k_i . k_s and q_i . k_s of the ancestor pairs, for a new key
+    // head: rounds of four column tiles J, whose K rows their owners
+    // broadcast through LDS; each wavefront multiplies them with its own row
+    // tiles I >= J that hold pairs
+    auto tree_gram = [&](int j) {
+        bf16x8* gbuf[4] = {gbuf0, gbuf1, reinterpret_cast<bf16x8*>(slot_base(j & 1)),
+                           reinterpret_cast<bf16x8*>(slot_base(j & 1) + L::GB_BYTES)};
+        const int NT = (N + 15) >> 4;
+        // this wavefront's row tiles: their tile-mask words and the path
+        // offsets of their rows
+        uint32_t tmr[RT];
+        int offr[RT][4];
 #pragma unroll
-                    for (int t = 0; t < KS; ++t) gb[t * 64 + lane] = (RT > 1 && J >= NWT) ? kf[RT - 1][t] : kf[0][t];
+        for (int u = 0; u < RT; ++u) {
+            tmr[u] = tmask[tile_of(u)];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) offr[u][rr] = off[16 * tile_of(u) + 4 * lg + rr];
+        }
+        for (int J0 = 0; J0 < NT; J0 += 4) {
+            if (J0 > 0) tree_sync();   // the previous round's tiles are read
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int J = J0 + v;
+                const int owner = J < NWT ? J : NTMAX - 1 - J;
+                if (J < NT && twave == owner) {
+#pragma unroll
+                    for (int t = 0; t < KS; ++t) gbuf[v][t * 64 + lane] = (RT > 1 && J >= NWT) ? kf[RT - 1][t] : kf[0][t];
                 }
-                tree_sync();
+            }
+            tree_sync();
+            if (J0 == 0) GDN_PHASE(0); else GDN_PHASE(7);
+            // the ancestor words of this wavefront's rows for the round's
+            // column tiles (node s = 16 J + lc sits in word J / 2)
+            uint32_t aw[RT][4][2];
+#pragma unroll
+            for (int u = 0; u < RT; ++u)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                    for (int x = 0; x < 2; ++x)
+                        aw[u][rr][x] = anc[(16 * tile_of(u) + 4 * lg + rr) * L::AW + min((J0 >> 1) + x, L::AW - 1)];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int J = J0 + v;
+                if (J >= NT) continue;
+                bf16x8 kb[KS];
+#pragma unroll
+                for (int t = 0; t < KS; ++t) kb[t] = gbuf[v][t * 64 + lane];
+                const int sn = 16 * J + lc;
+                const int ds = dep[sn];
 #pragma unroll
                 for (int u = 0; u < RT; ++u) {
                     const int I = tile_of(u);
-                    if (I >= J && I < NT && ((tmask[I] >> J) & 1u)) {
+                    if (I >= J && I < NT && ((tmr[u] >> J) & 1u)) {
                         f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int t = 0; t < KS; ++t) {
-                            const bf16x8 kb = gb[t * 64 + lane];
-                            akk = mfma(kf[u][t], kb, akk);
-                            aqk = mfma(qf[u][t], kb, aqk);
+                            akk = mfma(kf[u][t], kb[t], akk);
+                            aqk = mfma(qf[u][t], kb[t], aqk);
                         }
-                        const int sn = 16 * J + lc;
-                        const int ds = dep[sn];
-                        uint32_t aw[4];
-                        int oi[4];
+                        // entries that are not ancestor pairs go to the sink
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr) {
                             const int i = 16 * I + 4 * lg + rr;
-                            aw[rr] = anc[i * L::AW + (sn >> 5)];
-                            oi[rr] = off[i];
-                        }
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) {
-                            const int i = 16 * I + 4 * lg + rr;
-                            if (i < N && ((aw[rr] >> (sn & 31)) & 1u)) {
-                                const int p = oi[rr] + ds - 1;
-                                kk[p] = akk[rr];
-                                qk[p] = aqk[rr];
-                            }
+                            const bool pair = i < N && ((aw[u][rr][v >> 1] >> (sn & 31)) & 1u);
+                            const int p = pair ? offr[u][rr] + ds - 1 : L::CAP;
+                            kk[p] = akk[rr];
+                            qk[p] = aqk[rr];
                         }
                     }
                 }
             }
-            t_kh = kh;
+            if (J0 == 0) GDN_PHASE(4);
         }
+        t_kh = item_kh(j);
+    };
+    // X and Y, the rows of Z~, the pair positions
+    auto tree_tail = [&](int j) {
+        const int slot = j & 1;
+        const int total = t_total;
         tree_sync();
         GDN_PHASE(11);
         // X and Y per pair
-        float* ye = zout + slot * L::CAP;
+        float* ye = zout_s(slot);
         for (int p = ttid; p < total; p += TTH) {
             const int i = pnode[p], s = pathc[p];
             const float D = __expf(Gs[i] - Gs[s]);
@@ -522,11 +606,23 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
         }
         // the pair positions for the dense side
         for (int p = ttid; p < total; p += TTH) {
-            spath[slot * L::CAP + p] = pathc[p];
-            spnode[slot * L::CAP + p] = pnode[p];
+            spath_s(slot)[p] = pathc[p];
+            spnode_s(slot)[p] = pnode[p];
         }
         tree_sync();
         GDN_PHASE(13);
+    };
+    auto tree_item = [&](int j) {
+        const bool new_b = item_b(j) != t_b;
+        const bool new_kh = new_b || item_kh(j) != t_kh;
+        if (new_b) tree_struct(j);
+        if (!tree_check(j)) return;
+        if (new_kh) {
+            hold_kq(j);
+            tree_gram(j);
+        }
+        tree_g(j);
+        tree_tail(j);
     };
 
     // --------------------------------------------------------------- dense side
@@ -599,9 +695,11 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
         // 4 ((t >> 4) & 1) + (t & 3).  Items of one sequence write the same
         // positions, so no clearing is needed between them.
         {
-            const float* ze = zout + slot * L::CAP;
+            const float* ze = zout_s(slot);
+            const uint8_t* sp = spath_s(slot);
+            const uint8_t* sn = spnode_s(slot);
             for (int p = tid; p < total; p += 64 * NWD) {
-                const int i = spnode[slot * L::CAP + p], t = spath[slot * L::CAP + p];
+                const int i = sn[p], t = sp[p];
                 const float z = ze[p];
                 const __bf16 zh = static_cast<__bf16>(z);
                 const __bf16 zl = static_cast<__bf16>(z - static_cast<float>(zh));
@@ -614,7 +712,7 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
         dense_sync();
 
         GDN_PHASE(1);
-        const float* ge = gamd + slot * NMAX;
+        const float* ge = gamd_s(slot);
         const int NT = (N + 15) >> 4;
         bf16x8 s0h[CT][KS], s0l[CT][KS];
 #pragma unroll
@@ -740,19 +838,41 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
     auto new_kq_at = [&](int j) {
         return j > 0 && j < nit && (item_b(j) != item_b(j - 1) || item_kh(j) != item_kh(j - 1));
     };
+    // Start-up (first item): the tree side loads the scalars and builds the
+    // structure; meanwhile the dense side stages the first key head's K/Q
+    // straight into LDS, then issues its S0/V loads and computes every lower
+    // Gram tile from LDS, which it scatters into the pair list once the
+    // structure is known.  Workgroup barriers B1 .. B4 order the two.
+    constexpr int NTILE0 = NTMAX * (NTMAX + 1) / 2;
+    constexpr int GT0 = (NTILE0 + NWD - 1) / NWD;
+    auto tile_ij = [&](int t, int& I, int& J) {
+        I = 0;
+        while ((I + 1) * (I + 2) / 2 <= t) ++I;
+        J = t - I * (I + 1) / 2;
+    };
     if (is_tree) {
-        // the first item's scalars and K/Q go out before the dense side's
-        // S0/V, and the scalars are in before the dense side issues those
         load_scalars(0);
-        load_kq(0);
         tree_scalars(0);
-        __syncthreads();
-        tree_item(0);
+        __syncthreads();   // B1
+        tree_struct(0);
+        __syncthreads();   // B2
+        const bool ok0 = tree_check(0);
+        if (ok0) tree_g(0);
+        __syncthreads();   // B3: Gram values of the first key head are in
+        if (ok0) {
+            t_kh = item_kh(0);
+            tree_tail(0);
+        }
         load_scalars(min(1, nit - 1));
-        __syncthreads();
-        stage_kq();
-        __syncthreads();
-        if (new_kq_at(1)) load_kq(1);
+        __syncthreads();   // B4
+        // the next key head's K/Q go into the registers as soon as the
+        // current ones have been used (Gram and staging)
+        auto next_kq = [&](int j) {
+            int q = max(j, 1);
+            while (q < nit && !new_kq_at(q)) ++q;
+            return q;
+        };
+        if (next_kq(1) < nit) hold_kq(next_kq(1));
         GDN_PHASE(6);
         GDN_PHASE_SNAP;
         for (int j = 0; j < nit; ++j) {
@@ -763,30 +883,77 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
                 tree_item(j + 1);
             }
             load_scalars(min(j + 2, nit - 1));
+            GDN_PHASE_ARRIVE(j);
             if (restage) {
+                hold_kq(j + 1);   // held already unless a walk forced this
                 __syncthreads();
                 stage_kq();
                 __syncthreads();
             } else {
                 __syncthreads();
             }
-            if (new_kq_at(j + 2)) load_kq(j + 2);
+            if (next_kq(j + 2) < nit) hold_kq(next_kq(j + 2));
             GDN_PHASE(14);
+            GDN_PHASE_ITER(j);
         }
     } else {
-        __syncthreads();
-        load_sv(0, 1);
-        __syncthreads();
-        __syncthreads();
+        {
+            constexpr int NDT = 64 * NWD;
+            constexpr int KC0 = (NMAX * CH + NDT - 1) / NDT;
+            const int bb = item_b(0), kh = item_kh(0);
+            uint4 kv[KC0], qv[KC0];
+#pragma unroll
+            for (int q = 0; q < KC0; ++q) {
+                const int e = min(tid + q * NDT, NMAX * CH - 1);
+                const size_t gofs = ((static_cast<size_t>(bb) * N + min(e / CH, N - 1)) * Hk + kh) * DK + (e % CH) * 8;
+                kv[q] = *reinterpret_cast<const uint4*>(kg + gofs);
+                qv[q] = *reinterpret_cast<const uint4*>(qg + gofs);
+            }
+#pragma unroll
+            for (int q = 0; q < KC0; ++q) {
+                const int e = tid + q * NDT;
+                if (e < NMAX * CH) put_chunk(e / CH, e % CH, kv[q], qv[q]);
+            }
+        }
+        __syncthreads();   // B1
+        load_sv(0, 1);     // after the first key head's K/Q are in
+        f32x4 gk[GT0], gq[GT0];
+#pragma unroll
+        for (int u = 0; u < GT0; ++u) {
+            int I, J;
+            tile_ij(min(wave + NWD * u, NTILE0 - 1), I, J);
+            gk[u] = gq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 fb = frag(Ks, 16 * J + lc, ks);
+                gk[u] = mfma(frag(Ks, 16 * I + lc, ks), fb, gk[u]);
+                gq[u] = mfma(frag(Qs, 16 * I + lc, ks), fb, gq[u]);
+            }
+        }
+        __syncthreads();   // B2: the structure is built
+        if (misc[0] <= L::CAP) {
+            const int NT = (N + 15) >> 4;
+#pragma unroll
+            for (int u = 0; u < GT0; ++u) {
+                const int t = wave + NWD * u;
+                int I, J;
+                tile_ij(min(t, NTILE0 - 1), I, J);
+                if (t < NTILE0 && I < NT && ((tmask[I] >> J) & 1u)) put_pairs(I, J, gk[u], gq[u]);
+            }
+        }
+        __syncthreads();   // B3
+        __syncthreads();   // B4
         GDN_PHASE(7);
         GDN_PHASE_SNAP;
         for (int j = 0; j < nit; ++j) {
             refresh();
             const bool restage = restage_after(j);
             dense_item(j);
+            GDN_PHASE_ARRIVE(j);
             __syncthreads();
             if (restage) __syncthreads();
             GDN_PHASE(6);
+            GDN_PHASE_ITER(j);
         }
     }
     // a timed-out role barrier means the protocol above is broken: report it
@@ -799,21 +966,29 @@ __global__ __launch_bounds__(512) void verify_ws_kernel(VerifyArgs a, int items_
 
 }  // namespace
 
+#ifndef GDN_WS_DENSE_WAVES
+#define GDN_WS_DENSE_WAVES(dv) ((dv) / 16)
+#endif
+
 hipError_t launch_verify_ws(const VerifyArgs& a, hipStream_t stream) {
     const int items = a.B * a.H_v;
     const int wgs = min(items, device_cus());
     const int per = (items + wgs - 1) / wgs;
     const dim3 grid((items + per - 1) / per);
-    auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(512), 0, stream, a, per);
+    auto go = [&](auto kern, int dv) {
+        hipLaunchKernelGGL(kern, grid, dim3(64 * (GDN_WS_DENSE_WAVES(dv) + 4)), 0, stream, a, per);
         return hipGetLastError();
     };
+    // dense wavefronts: one per 16 value columns
+    constexpr int W64 = GDN_WS_DENSE_WAVES(64), W128 = GDN_WS_DENSE_WAVES(128);
     if (a.N <= 64) {
-        if (a.d_k == 64) return a.d_v == 64 ? go(verify_ws_kernel<64, 64, 64>) : go(verify_ws_kernel<64, 64, 128>);
-        return a.d_v == 64 ? go(verify_ws_kernel<64, 128, 64>) : go(verify_ws_kernel<64, 128, 128>);
+        if (a.d_k == 64)
+            return a.d_v == 64 ? go(verify_ws_kernel<64, 64, 64, W64>, 64) : go(verify_ws_kernel<64, 64, 128, W128>, 128);
+        return a.d_v == 64 ? go(verify_ws_kernel<64, 128, 64, W64>, 64) : go(verify_ws_kernel<64, 128, 128, W128>, 128);
     }
-    if (a.d_k == 64) return a.d_v == 64 ? go(verify_ws_kernel<128, 64, 64>) : go(verify_ws_kernel<128, 64, 128>);
-    return a.d_v == 64 ? go(verify_ws_kernel<128, 128, 64>) : go(verify_ws_kernel<128, 128, 128>);
+    if (a.d_k == 64)
+        return a.d_v == 64 ? go(verify_ws_kernel<128, 64, 64, W64>, 64) : go(verify_ws_kernel<128, 64, 128, W128>, 128);
+    return a.d_v == 64 ? go(verify_ws_kernel<128, 128, 64, W64>, 64) : go(verify_ws_kernel<128, 128, 128, W128>, 128);
 }
 
 }  // namespace gdn
