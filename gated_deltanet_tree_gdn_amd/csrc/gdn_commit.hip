@@ -111,13 +111,24 @@ __global__ __launch_bounds__(256, 4) void commit_mfma_kernel(CommitArgs a) {
     __syncthreads();
     const int m = misc_s[1];
 
-    // Gates along the path, cumulative within each chunk.
-    if (tid < m) {
-        const int c0 = tid & ~(kChunk - 1);
-        float G = 0.f;
-        for (int t = c0; t <= tid; ++t) G += a.g[(static_cast<size_t>(b) * N + path_s[m - 1 - t]) * Hv + h];
-        gl_s[tid] = G;
-        bl_s[tid] = a.beta[(static_cast<size_t>(b) * N + path_s[m - 1 - tid]) * Hv + h];
+    // Gates along the path, cumulative within each chunk: one load per
+    // path node, then an inclusive scan over the chunk's 16 lanes.
+    {
+        float G = 0.f, bt = 0.f;
+        if (tid < m) {
+            const size_t nh = (static_cast<size_t>(b) * N + path_s[m - 1 - tid]) * Hv + h;
+            G = a.g[nh];
+            bt = a.beta[nh];
+        }
+#pragma unroll
+        for (int o = 1; o < kChunk; o <<= 1) {
+            const float x = __shfl_up(G, o, kChunk);
+            if ((l & (kChunk - 1)) >= o) G += x;
+        }
+        if (tid < m) {
+            gl_s[tid] = G;
+            bl_s[tid] = bt;
+        }
     }
 
     auto stage = [&](int c0, int n) {
