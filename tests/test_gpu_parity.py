@@ -372,6 +372,11 @@ def _mixed_depth_inputs(cfg, seed, chain_every):
     dict(B=40, N=128, H_k=3, H_v=9),      # 2 heads per workgroup, sequence and key-head changes inside one
     dict(B=24, N=64, H_k=4, H_v=16),      # N <= 64 layout, 2 heads per workgroup
     dict(B=33, N=100, H_k=16, H_v=32),    # 5 heads per workgroup, ragged last workgroup
+    dict(B=40, N=77, H_k=3, H_v=9, d_k=64, d_v=64),
+    dict(B=40, N=128, H_k=9, H_v=9, d_k=64, d_v=128),
+    dict(B=40, N=50, H_k=1, H_v=9, d_k=128, d_v=64),
+    dict(B=300, N=1, H_k=1, H_v=2),       # single-node trees, 3 heads per workgroup
+    dict(B=64, N=17, H_k=2, H_v=8),       # one node past a 16-node tile
 ])
 def test_pipeline_item_boundaries(shape, lockstep, monkeypatch):
     """several (sequence, head) items per persistent workgroup: sequence,
