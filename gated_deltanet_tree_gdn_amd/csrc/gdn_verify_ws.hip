@@ -66,8 +66,8 @@ __host__ __device__ constexpr int ws_align(int x, int a) { return (x + a - 1) / 
 template <int NMAX, int DK>
 struct WsLds {
     // pair-list capacity: every tree of N <= 64 fits; for N <= 128 the
-    // paths may sum to 1536 nodes (12 per node on average)
-    static constexpr int CAP = NMAX <= 64 ? NMAX * (NMAX + 1) / 2 : 1536;
+    // paths may sum to 2048 nodes, which holds every tree of depth <= 16
+    static constexpr int CAP = NMAX <= 64 ? NMAX * (NMAX + 1) / 2 : 2048;
     static constexpr int AW = NMAX / 32;
     // dense side
     static constexpr int KQ_BYTES = NMAX * DK * 2;
@@ -77,23 +77,21 @@ struct WsLds {
     static constexpr int ZD_BYTES = 2048 * ws_zblocks(NMAX / 16);
     // hand-over slots (tree side writes slot (j+1)&1, dense side reads j&1)
     // hand-over slots s = 0, 1, each: float[CAP] Y, then the rows of Z~;
-    // float[NMAX] gamma (0 past N); uint8[CAP] ancestor and uint8[CAP] node
-    // of each pair
-    static constexpr int SLOT = ws_align(4 * CAP + 4 * NMAX + 2 * CAP, 16);
+    // float[NMAX] gamma (0 past N).  The pair positions (ancestor and node
+    // of each pair) are the tree side's own arrays, which it rewrites for a
+    // new sequence only once the dense side has scattered its last item.
+    static constexpr int SLOT = ws_align(4 * CAP + 4 * NMAX, 16);
     static constexpr int SLOTS = ZD + ZD_BYTES;
     static constexpr int S_GAM = 4 * CAP;
-    static constexpr int S_PATH = S_GAM + 4 * NMAX;
-    static constexpr int S_NODE = S_PATH + CAP;
-    static constexpr int SPNODE_END = SLOTS + 2 * SLOT;
+    static constexpr int SLOTS_END = SLOTS + 2 * SLOT;
     // tree side
-    static constexpr int XC = ws_align(SPNODE_END, 16);  // float[CAP + 16]: X (zero pads)
+    static constexpr int XC = ws_align(SLOTS_END, 16);  // float[CAP + 16]: X (zero pads)
     // float[CAP + 4]: k_i . k_s and q_i . k_s per key head (entry CAP takes
     // the Gram tile entries that are not ancestor pairs)
     static constexpr int KK = XC + 4 * (CAP + 16);
     static constexpr int QK = KK + 4 * (CAP + 4);
-    static constexpr int OFP = QK + 4 * (CAP + 4);   // uint16[CAP]: path offset of the ancestor
-    static constexpr int PATH = OFP + 2 * CAP;       // uint8[CAP]
-    static constexpr int PNODE = PATH + CAP;         // uint8[CAP]
+    static constexpr int PATH = QK + 4 * (CAP + 4);  // uint8[CAP]: the root..i path of every node i
+    static constexpr int PNODE = PATH + CAP;         // uint8[CAP]: node i owning each pair
     static constexpr int NODE = ws_align(PNODE + CAP, 16);
     static constexpr int PAR = NODE;                 // int[NMAX]
     static constexpr int DEP = PAR + 4 * NMAX;
@@ -117,7 +115,7 @@ struct WsLds {
     static constexpr int TOTAL = GB1 + GB_BYTES;
     // misc[]: 0 tree total, 2 dense sync counter, 3 tree sync counter,
     // 4 spin time-outs, 5/6 slot pair totals, 7/8 slot fallback flags,
-    // 9 invalid-parent flag
+    // 9 invalid-parent flag, 10 items the dense side has scattered
     // the fallback walk (dense side) overwrites K/Q and the fragments:
     // u [NMAX][64], S0 slice [DK][64], k and q rows, G, parents
     static constexpr int FB_S0 = NMAX * 64 * 4;
@@ -140,6 +138,17 @@ __device__ __forceinline__ void role_sync(int* ctr, int nwaves, int& count, int*
     const int target = count * nwaves;
     for (int spins = 0; __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target; ++spins) {
         // after one time-out the counts no longer match: stop waiting
+        if (spins > (1 << 22) || __hip_atomic_load(timeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
+            __hip_atomic_store(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            break;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wait until the LDS counter `ctr` reaches `target` (bounded like role_sync).
+__device__ __forceinline__ void role_wait(int* ctr, int target, int* timeouts) {
+    for (int spins = 0; __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target; ++spins) {
         if (spins > (1 << 22) || __hip_atomic_load(timeouts, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
             __hip_atomic_store(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             break;
@@ -208,12 +217,9 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
     auto slot_base = [&](int sl) { return smem + L::SLOTS + sl * L::SLOT; };
     auto zout_s = [&](int sl) { return reinterpret_cast<float*>(slot_base(sl)); };
     auto gamd_s = [&](int sl) { return reinterpret_cast<float*>(slot_base(sl) + L::S_GAM); };
-    auto spath_s = [&](int sl) { return slot_base(sl) + L::S_PATH; };
-    auto spnode_s = [&](int sl) { return slot_base(sl) + L::S_NODE; };
     float* xc = reinterpret_cast<float*>(smem + L::XC);
     float* kk = reinterpret_cast<float*>(smem + L::KK);
     float* qk = reinterpret_cast<float*>(smem + L::QK);
-    uint16_t* ofp = reinterpret_cast<uint16_t*>(smem + L::OFP);
     uint8_t* pathc = smem + L::PATH;
     uint8_t* pnode = smem + L::PNODE;
     int* par = reinterpret_cast<int*>(smem + L::PAR);
@@ -236,6 +242,14 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
     int dsync = 0, tsync = 0;
     auto dense_sync = [&]() { role_sync(misc + 2, NWD, dsync, misc + 4); };
     auto tree_sync = [&]() { role_sync(misc + 3, NWT, tsync, misc + 4); };
+    // the dense side counts the items whose pair positions it has read
+    auto dense_scattered = [&]() {
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __hip_atomic_fetch_add(misc + 10, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    };
+    auto wait_scattered = [&](int n) { role_wait(misc + 10, n, misc + 4); };
 
     // ---------------------------------------------------------------- tree side
     // K and Q of an item's key head live in the tree wavefronts' registers,
@@ -400,6 +414,9 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
             GDN_PHASE(3);
             if (h == 0 && ttid == 0) a.tree_status[b] = misc[9] ? GDN_ERR_TREE : 0;
             t_total = misc[0];
+            // the dense side reads the previous sequence's pair positions
+            // at the start of its item j - 1
+            if (j > 0) wait_scattered(j);
             if (t_total <= L::CAP && ttid < NMAX) {
                 const int i = ttid;
                 uint32_t bits[L::AW];
@@ -411,7 +428,6 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
                     for (int s = i; s >= 0; s = par[s]) {
                         pathc[pos] = static_cast<uint8_t>(s);
                         pnode[pos] = static_cast<uint8_t>(i);
-                        ofp[pos] = static_cast<uint16_t>(off[s]);
                         --pos;
                         mask |= 1u << (s >> 4);
 #pragma unroll
@@ -574,7 +590,7 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
                 for (int bb = 0; bb < ZR; ++bb) {
                     const int pp = o + min(bb, m - 1);
                     tt[bb] = pathc[pp];
-                    oa[bb] = ofp[pp];
+                    oa[bb] = off[tt[bb]];
                     z[bb] = bb < m ? ye[pp] : 0.f;
                 }
                 float xr[ZR - 1];
@@ -598,16 +614,11 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
             } else {
                 for (int aa = m - 1; aa >= 1; --aa) {
                     const float za = ye[o + aa];
-                    const int oa = ofp[o + aa];
+                    const int oa = off[pathc[o + aa]];
                     for (int bb = 0; bb < aa; ++bb) ye[o + bb] -= za * xc[oa + bb];
                 }
                 for (int bb = 0; bb < m; ++bb) ye[o + bb] *= bet[pathc[o + bb]];
             }
-        }
-        // the pair positions for the dense side
-        for (int p = ttid; p < total; p += TTH) {
-            spath_s(slot)[p] = pathc[p];
-            spnode_s(slot)[p] = pnode[p];
         }
         tree_sync();
         GDN_PHASE(13);
@@ -665,6 +676,7 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
         if (L::HAS_FALLBACK && misc[7 + slot]) {
             // deep tree: the per-node walk by dense wavefront 0 (the others
             // go on to the next item's loads and wait at the item barrier)
+            dense_scattered();
             __builtin_amdgcn_s_waitcnt(0);   // this item's S0/V loads are unused
             if (wave == 0) {
                 int* par_s = reinterpret_cast<int*>(smem + L::FB_PAR);
@@ -696,8 +708,8 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
         // positions, so no clearing is needed between them.
         {
             const float* ze = zout_s(slot);
-            const uint8_t* sp = spath_s(slot);
-            const uint8_t* sn = spnode_s(slot);
+            const uint8_t* sp = pathc;
+            const uint8_t* sn = pnode;
             for (int p = tid; p < total; p += 64 * NWD) {
                 const int i = sn[p], t = sp[p];
                 const float z = ze[p];
@@ -710,6 +722,7 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
             }
         }
         dense_sync();
+        dense_scattered();
 
         GDN_PHASE(1);
         const float* ge = gamd_s(slot);

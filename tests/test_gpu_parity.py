@@ -390,3 +390,37 @@ def test_pipeline_item_boundaries(shape, lockstep, monkeypatch):
     o, ctx = run_verify(d)
     gdn.gdn_ctx_status(ctx)
     assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), f"pipeline {shape} o")
+
+
+def _spine_tree(N, k, extra):
+    """a chain of k nodes, every other node a child of the chain's last
+    node, and the last `extra` of those one level deeper (under node k):
+    paths that sum to k(k+1)/2 + (N-k)(k+1) + extra nodes"""
+    par = np.empty(N, dtype=np.int32)
+    par[0] = -1
+    par[1:k] = np.arange(0, k - 1)
+    par[k:] = k - 1
+    par[N - extra:] = k
+    return par
+
+
+@pytest.mark.parametrize("lockstep", [0, 1])
+def test_pair_list_capacity_boundary(lockstep, monkeypatch):
+    """N = 128 trees whose paths sum to 1928 (the most a depth-16 tree can
+    reach), 2048 and 2049 nodes, between best-first trees: the MFMA path's
+    pair list must hold the first two, the third takes the per-node walk"""
+    if lockstep:
+        monkeypatch.setenv("GDN_VERIFY_LOCKSTEP", "1")
+    cfg = G.shrink(G.CONFIGS["bestfirst_b32n128"], B=8, H_k=2, H_v=4)
+    inp = G.make_inputs(cfg, seed=5)
+    par = inp["parent"].copy()
+    for b, (k, extra) in {1: (15, 0), 2: (16, 8), 4: (16, 9), 5: (16, 8)}.items():
+        par[b] = _spine_tree(cfg.N, k, extra)
+    totals = [int(t) for t in oracle.ancestors(par)[1].sum(axis=1)]
+    assert totals[1] == 1928 and totals[2] == 2048 and totals[4] == 2049
+    inp["parent"] = par
+    d = G.to_device(inp)
+    say(f"[capacity] path totals {totals} lockstep={lockstep}")
+    o, ctx = run_verify(d)
+    gdn.gdn_ctx_status(ctx)
+    assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), "capacity boundary o")
