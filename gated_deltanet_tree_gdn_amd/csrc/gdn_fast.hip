@@ -73,8 +73,8 @@ template <int NMAX, int DK>
 struct Lds {
     static constexpr bool DENSE = NMAX <= 128;
     // pair-list capacity: every tree of N <= 64 fits; N <= 128 covers depth
-    // <= 16 everywhere; N <= 256 covers 16 ancestors per node on average
-    static constexpr int CAP = NMAX <= 64 ? NMAX * (NMAX + 1) / 2 : (NMAX <= 128 ? 2048 : 4096);
+    // <= 16 everywhere, N <= 256 depth <= 24
+    static constexpr int CAP = NMAX <= 64 ? NMAX * (NMAX + 1) / 2 : (NMAX <= 128 ? 2048 : 6144);
     static constexpr int AW = NMAX / 32;        // ancestor bit-row words
     static constexpr int KROW = DK * 2 + 16;    // staged k / q row, padded against bank conflicts
     static constexpr int KS_OFF = 0;
@@ -88,8 +88,7 @@ struct Lds {
     static constexpr int QK = KK + (KEEP_GRAM ? 4 * CAP : 0);  // float[CAP]: q_i . k_s
     static constexpr int XC = QK + (KEEP_GRAM ? 4 * CAP : 0);  // float[CAP]: X (per value head)
     static constexpr int YC = XC + 4 * (CAP + 16);  // float[CAP]: Y, then the rows of Z~ (X has 16 zero pads)
-    static constexpr int OFP = YC + 4 * CAP;    // uint16[CAP]: path offset of the ancestor
-    static constexpr int PATH = OFP + 2 * CAP;  // uint8[CAP]: root..i path of every node
+    static constexpr int PATH = YC + 4 * CAP;   // uint8[CAP]: root..i path of every node
     static constexpr int PNODE = PATH + CAP;    // uint8[CAP]: node owning each pair
     static constexpr int NODE = (PNODE + CAP + 15) & ~15;
     static constexpr int PAR = NODE;            // int[NMAX]
@@ -157,7 +156,6 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
     float* yc = reinterpret_cast<float*>(smem + L::YC);
     float* kk = L::KEEP_GRAM ? reinterpret_cast<float*>(smem + L::KK) : xc;
     float* qk = L::KEEP_GRAM ? reinterpret_cast<float*>(smem + L::QK) : yc;
-    uint16_t* ofp = reinterpret_cast<uint16_t*>(smem + L::OFP);
     uint8_t* pathc = smem + L::PATH;
     uint8_t* pnode = smem + L::PNODE;
     unsigned char* Ks = smem + L::KS_OFF;
@@ -335,7 +333,6 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
                         for (int s = i; s >= 0; s = par[s]) {
                             pathc[pos] = static_cast<uint8_t>(s);
                             pnode[pos] = static_cast<uint8_t>(i);
-                            ofp[pos] = static_cast<uint16_t>(off[s]);
                             --pos;
                             mask |= 1u << (s >> 4);
 #pragma unroll
@@ -482,7 +479,7 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
                 for (int bb = 0; bb < ZR; ++bb) {
                     const int pp = o + min(bb, m - 1);
                     t[bb] = pathc[pp];
-                    oa[bb] = ofp[pp];
+                    oa[bb] = off[t[bb]];
                     z[bb] = bb < m ? yc[pp] : 0.f;
                 }
                 // one row of X in flight ahead of the row being applied
@@ -528,7 +525,7 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
             }
             for (int aa = m - 1; aa >= 1; --aa) {
                 const float za = yc[o + aa];
-                const int oa = ofp[o + aa];
+                const int oa = off[pathc[o + aa]];
                 for (int bb = 0; bb < aa; ++bb) yc[o + bb] -= za * xc[oa + bb];
             }
             for (int bb = 0; bb < m; ++bb) yc[o + bb] *= bet[pathc[o + bb]];

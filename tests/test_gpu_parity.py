@@ -404,23 +404,29 @@ def _spine_tree(N, k, extra):
     return par
 
 
+@pytest.mark.parametrize("N,spines,expect", [
+    (128, {1: (15, 0), 2: (16, 8), 4: (16, 9), 5: (16, 8)}, {1: 1928, 2: 2048, 4: 2049}),
+    (256, {0: (23, 0), 3: (24, 44), 4: (24, 45)}, {0: 5868, 3: 6144, 4: 6145}),
+])
 @pytest.mark.parametrize("lockstep", [0, 1])
-def test_pair_list_capacity_boundary(lockstep, monkeypatch):
-    """N = 128 trees whose paths sum to 1928 (the most a depth-16 tree can
-    reach), 2048 and 2049 nodes, between best-first trees: the MFMA path's
-    pair list must hold the first two, the third takes the per-node walk"""
+def test_pair_list_capacity_boundary(N, spines, expect, lockstep, monkeypatch):
+    """trees whose paths sum to the most a best-first tree of the pages'
+    depth reaches (1928 nodes at N = 128, depth 16; 5868 at N = 256, depth
+    24), to the pair-list capacity of the MFMA kernels (2048, 6144) and one
+    past it, between best-first trees: the first two stay on the MFMA path,
+    the last takes the per-node walk"""
     if lockstep:
         monkeypatch.setenv("GDN_VERIFY_LOCKSTEP", "1")
-    cfg = G.shrink(G.CONFIGS["bestfirst_b32n128"], B=8, H_k=2, H_v=4)
+    cfg = G.shrink(G.CONFIGS["bestfirst_b32n128"], B=6, N=N, H_k=2, H_v=4)
     inp = G.make_inputs(cfg, seed=5)
     par = inp["parent"].copy()
-    for b, (k, extra) in {1: (15, 0), 2: (16, 8), 4: (16, 9), 5: (16, 8)}.items():
+    for b, (k, extra) in spines.items():
         par[b] = _spine_tree(cfg.N, k, extra)
     totals = [int(t) for t in oracle.ancestors(par)[1].sum(axis=1)]
-    assert totals[1] == 1928 and totals[2] == 2048 and totals[4] == 2049
+    assert all(totals[b] == t for b, t in expect.items()), totals
     inp["parent"] = par
     d = G.to_device(inp)
-    say(f"[capacity] path totals {totals} lockstep={lockstep}")
+    say(f"[capacity] N={N} path totals {totals} lockstep={lockstep}")
     o, ctx = run_verify(d)
     gdn.gdn_ctx_status(ctx)
     assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), "capacity boundary o")
