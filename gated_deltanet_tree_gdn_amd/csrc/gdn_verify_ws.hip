@@ -820,11 +820,12 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
                         acc[st] = mfma(rh[st][kap], zl, acc[st]);
                     }
                 }
+                // o is written once and not read back here: streaming stores
                 const int i = 16 * I + lc;
                 if (i < N) {
 #pragma unroll
                     for (int st = 0; st < CT; ++st)
-                        *reinterpret_cast<f32x4*>(obase + static_cast<size_t>(i) * Hv * DV + 16 * st) = acc[st];
+                        __builtin_nontemporal_store(acc[st], reinterpret_cast<f32x4*>(obase + static_cast<size_t>(i) * Hv * DV + 16 * st));
                 }
             }
         }
@@ -853,9 +854,12 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
     };
     // Start-up (first item): the tree side loads the scalars and builds the
     // structure; meanwhile the dense side stages the first key head's K/Q
-    // straight into LDS, then issues its S0/V loads and computes every lower
-    // Gram tile from LDS, which it scatters into the pair list once the
-    // structure is known.  Workgroup barriers B1 .. B4 order the two.
+    // straight into LDS and computes every lower Gram tile from LDS, which it
+    // scatters into the pair list once the structure is known.  Its S0/V
+    // loads go out only while the tree side solves for the first item: the
+    // memory queue is then free of the start-up's own loads, which would
+    // otherwise hold up the Gram tiles behind them.  Workgroup barriers
+    // B1 .. B4 order the two.
     constexpr int NTILE0 = NTMAX * (NTMAX + 1) / 2;
     constexpr int GT0 = (NTILE0 + NWD - 1) / NWD;
     auto tile_ij = [&](int t, int& I, int& J) {
@@ -929,7 +933,6 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
             }
         }
         __syncthreads();   // B1
-        load_sv(0, 1);     // after the first key head's K/Q are in
         f32x4 gk[GT0], gq[GT0];
 #pragma unroll
         for (int u = 0; u < GT0; ++u) {
@@ -955,6 +958,7 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
             }
         }
         __syncthreads();   // B3
+        load_sv(0, 1);
         __syncthreads();   // B4
         GDN_PHASE(7);
         GDN_PHASE_SNAP;
