@@ -138,7 +138,13 @@ def cpu_baseline(sets0, cfg, max_seqs):
         oracle.commit_inputs(host, accepted=acc, threads=threads)
         reps += 1
     dt = time.perf_counter() - t0
-    return {"value": reps * nb * cfg.N * cfg.H_v / dt, "unit": "nodes·heads/s", "cores": threads,
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
+    return {"value": reps * nb * cfg.N * cfg.H_v / dt, "unit": "nodes·heads/s", "cores": threads, "cpu": cpu,
             "kind": "oracle",
             "sample": f"fp64 oracle (per-path replay), verify + commit of sequences 0..{nb - 1} of input "
                       f"set 0 ({nb}x{cfg.N} nodes x {cfg.H_v} heads), {reps} repetitions on {threads} "
@@ -272,6 +278,22 @@ def main():
 
     verify_ms = timed(verify, args.steps)
     commit_ms = timed(commit, args.steps)
+
+    # per-call distribution: a HIP event pair around each call
+    def per_call(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            fn(sets[i % len(sets)])
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        return {"median_us": float(np.median(us)), "p10_us": float(np.percentile(us, 10)),
+                "p90_us": float(np.percentile(us, 90)), "calls": n}
+
+    verify_dist = per_call(verify, args.steps)
+    commit_dist = per_call(commit, args.steps)
     for s in sets:
         gdn.gdn_ctx_status(s["ctx"])
 
@@ -302,8 +324,9 @@ def main():
                    "arithmetic": "bf16 MFMA with fp32 accumulation; fp32 operands as bf16 hi+lo pairs; "
                                  "fp32 VALU for gates and the triangular solves"},
         "verify": {"ms": verify_ms, "nodes_heads_per_s": nh / (verify_ms * 1e-3),
-                   "algorithmic_bytes": vbytes, "GBps": achieved},
-        "commit": {"ms": commit_ms, "algorithmic_bytes": cbytes, "GBps": cbytes / (commit_ms * 1e-3) / 1e9,
+                   "algorithmic_bytes": vbytes, "GBps": achieved, "per_call": verify_dist},
+        "commit": {"ms": commit_ms, "per_call": commit_dist, "algorithmic_bytes": cbytes,
+                   "GBps": cbytes / (commit_ms * 1e-3) / 1e9,
                    "frac": cbytes / (commit_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": read_traffic("commit")},
         "roofline": {"bound": "hbm", "kernel": "gdn_tree_verify", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
