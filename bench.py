@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "GDN tree-verify nodes·heads/s per layer at B=32,N=128; % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 WORKLOAD = "bestfirst_b32n128"
 KERNEL_SOURCES = ["gdn_tree_api.cpp", "gdn_internal.h", "gdn_mfma.h", "gdn_walk.h", "gdn_simple.hip",
                   "gdn_fast.hip", "gdn_verify_grp.hip", "gdn_verify_ws.hip", "gdn_commit.hip"]
@@ -53,6 +54,15 @@ def verify_bytes(cfg) -> int:
     e = 2 if cfg.dtype == "bf16" else 4
     return (B * Hv * dv * dk * 4 + B * N * Hv * dv * 4 + B * N * Hv * dv * e
             + 2 * B * N * Hk * dk * e + 2 * B * N * Hv * 4 + B * N * 4)
+
+
+def verify_flops(cfg, mean_strict_ancestors) -> float:
+    """Algorithmic floating-point operations of one verify: per (node, value
+    head) 4 d_v d_k for S0 k_i and S0 q_i, plus 2 (d_k + d_v) (2 a + 1) for
+    the ancestor dot products and the solve and output updates, with a the
+    node's strict-ancestor count (its mean over the trees)."""
+    nh = cfg.B * cfg.N * cfg.H_v
+    return nh * (4.0 * cfg.d_v * cfg.d_k + 2.0 * (cfg.d_k + cfg.d_v) * (2.0 * mean_strict_ancestors + 1.0))
 
 
 def commit_bytes(cfg, path_len) -> int:
@@ -301,6 +311,7 @@ def main():
     vbytes = verify_bytes(cfg)
     cbytes = float(np.mean([commit_bytes(cfg, pl) for pl in path_lens]))
     achieved = vbytes / (verify_ms * 1e-3) / 1e9
+    vflops = verify_flops(cfg, float(np.mean([a["mean_strict_ancestors"] for a in anc_depth])))
     traffic = read_traffic("verify")
     out = {
         "metric": METRIC,
@@ -331,6 +342,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gdn_tree_verify", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic},
+        "mfma_secondary": {"kernel": "gdn_tree_verify", "algorithmic_flop": vflops,
+                           "achieved": vflops / (verify_ms * 1e-3) / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": vflops / (verify_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
         "wall_s_timed_region": wall,
     }
     if args.cpu_seqs > 0:
