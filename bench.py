@@ -148,6 +148,13 @@ def cpu_baseline(sets0, cfg, max_seqs):
         oracle.commit_inputs(host, accepted=acc, threads=threads)
         reps += 1
     dt = time.perf_counter() - t0
+    # the same oracle on one thread, over a smaller sample
+    n1 = min(4, nb)
+    one = {n: a[:n1] for n, a in host.items()}
+    t1 = time.perf_counter()
+    oracle.verify_inputs(one, threads=1)
+    oracle.commit_inputs(one, accepted=acc[:n1], threads=1)
+    dt1 = time.perf_counter() - t1
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -156,9 +163,11 @@ def cpu_baseline(sets0, cfg, max_seqs):
         pass
     return {"value": reps * nb * cfg.N * cfg.H_v / dt, "unit": "nodes·heads/s", "cores": threads, "cpu": cpu,
             "kind": "oracle",
-            "sample": f"fp64 oracle (per-path replay), verify + commit of sequences 0..{nb - 1} of input "
-                      f"set 0 ({nb}x{cfg.N} nodes x {cfg.H_v} heads), {reps} repetitions on {threads} "
-                      f"threads, {dt:.2f} s wall"}
+            "sample": f"fp64 oracle (memoised recurrence, bitwise equal to its per-path replay), verify + "
+                      f"commit of sequences 0..{nb - 1} of input set 0 ({nb}x{cfg.N} nodes x {cfg.H_v} heads), "
+                      f"{reps} repetitions on {threads} threads, {dt:.2f} s wall",
+            "single_thread": {"value": n1 * cfg.N * cfg.H_v / dt1, "unit": "nodes·heads/s", "cores": 1,
+                              "sample": f"sequences 0..{n1 - 1}, one repetition, {dt1:.2f} s wall"}}
 
 
 def main():
@@ -304,6 +313,20 @@ def main():
 
     verify_dist = per_call(verify, args.steps)
     commit_dist = per_call(commit, args.steps)
+
+    # context: a plain device copy (torch), read + write of 256 MiB each
+    src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record(stream)
+    for _ in range(20):
+        dst.copy_(src)
+    b_ev.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 20 * 2 * src.numel() * 4 / (a_ev.elapsed_time(b_ev) * 1e-3) / 1e9
+    del src, dst
     for s in sets:
         gdn.gdn_ctx_status(s["ctx"])
 
@@ -345,6 +368,8 @@ def main():
         "mfma_secondary": {"kernel": "gdn_tree_verify", "algorithmic_flop": vflops,
                            "achieved": vflops / (verify_ms * 1e-3) / 1e12, "peak": BF16_MFMA_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": vflops / (verify_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
+        "device_copy": {"GBps": copy_gbps, "bytes_per_copy": 2 * (64 << 20) * 4,
+                        "note": "torch copy_ of 256 MiB, read + write; context for the 8 TB/s peak"},
         "wall_s_timed_region": wall,
     }
     if args.cpu_seqs > 0:

@@ -430,3 +430,25 @@ def test_pair_list_capacity_boundary(N, spines, expect, lockstep, monkeypatch):
     o, ctx = run_verify(d)
     gdn.gdn_ctx_status(ctx)
     assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), "capacity boundary o")
+
+
+def test_side_stream():
+    """verify and commit launched on a stream other than the current one
+    (default priority), ordered only by that stream"""
+    cfg = G.shrink(G.CONFIGS["bestfirst_b32n128"], B=4, H_k=2, H_v=4)
+    inp = G.make_inputs(cfg, seed=21)
+    d = G.to_device(inp)
+    acc_np = np.array([cfg.N - 1, 0, -1, 37], dtype=np.int32)
+    acc = torch.from_numpy(acc_np).to("cuda:0")
+    ctx = gdn.GdnContext.for_tensors(d["q"], d["v"], d["parent"])
+    o = torch.empty((cfg.B, cfg.N, cfg.H_v, cfg.d_v), dtype=torch.float32, device="cuda:0")
+    S_new = torch.empty_like(d["S0"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())   # inputs and outputs allocated and filled
+    say("[side stream] verify + commit")
+    gdn.gdn_tree_verify(ctx, d["q"], d["k"], d["v"], d["g"], d["beta"], d["parent"], d["S0"], o=o, stream=side)
+    gdn.gdn_commit_path(ctx, acc, S_new=S_new, stream=side)
+    gdn.gdn_ctx_status(ctx, stream=side)
+    side.synchronize()
+    assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), "side-stream o")
+    assert_close(S_new.cpu().numpy(), oracle.commit_inputs(inp, accepted=acc_np), "side-stream S_new")
