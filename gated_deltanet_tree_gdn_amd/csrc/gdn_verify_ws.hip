@@ -10,22 +10,23 @@
 //     O = gamma o (Q S0^T) + Z~ R',
 // with Z~ built one row per node by back-substitution along its root path.
 //
-// One persistent workgroup of 8 wavefronts per compute unit takes a run of
-// (sequence b, value head h) items.  Two roles:
-//  - tree wavefronts (4-7) prepare item j+1: node scalars; for a new
-//    sequence the tree structure (depth, root paths, ancestor bits, the
+// One persistent workgroup per compute unit takes a run of (sequence b,
+// value head h) items, with d_v / 16 dense wavefronts (8 at d_v = 128, two
+// per SIMD) and 4 tree wavefronts.  Two roles:
+//  - tree wavefronts (the last four) prepare item j+1: node scalars; for a
+//    new sequence the tree structure (depth, root paths, ancestor bits, the
 //    16 x 16 tiles holding ancestor pairs); for a new key head the Gram
 //    values k_i . k_s and q_i . k_s of the pairs (MFMA; K and Q of the key
-//    head sit in these wavefronts' registers, two row tiles each, and one
-//    column tile at a time is broadcast through LDS); the gates G, gamma;
+//    head sit in these wavefronts' registers, two row tiles each, and four
+//    column tiles at a time are broadcast through LDS); the gates G, gamma;
 //    X and Y; the rows of Z~.  Results go to one of two LDS slots.  The same
 //    K/Q registers are written to LDS, in the dense side's fragment order,
 //    when the dense side moves to the new key head;
-//  - dense wavefronts (0-3) finish item j meanwhile: its Z~ (from the other
-//    slot) scattered into dense MFMA fragments, then per wavefront d_v / 4
-//    value columns: S0 split into bf16 hi + lo, K S0^T -> R', and per
-//    16-node tile gamma o (S0 Q^T) + R'^T Z~^T (transposed, so a lane stores
-//    16 contiguous bytes).
+//  - dense wavefronts finish item j meanwhile: its Z~ (from the other slot)
+//    scattered into dense MFMA fragments, then per wavefront 16 value
+//    columns: S0 split into bf16 hi + lo, K S0^T -> R', and per 16-node tile
+//    gamma o (S0 Q^T) + R'^T Z~^T (transposed, so a lane stores 16
+//    contiguous bytes).
 // The roles meet once per item at a workgroup barrier (twice when K/Q
 // change); inside a role the wavefronts synchronise through an LDS counter
 // (a bounded spin: a fault in the protocol ends the wait instead of hanging
