@@ -103,7 +103,9 @@ struct Lds {
     static constexpr int TMASK = ANC + 4 * AW * NMAX;  // uint32[NMAX/16]: tile (I, J) has pairs
     static constexpr int MISC = TMASK + 4 * (NMAX / 16);
     static constexpr int FBKQ = MISC + 64;      // float[2*DK] for the fallback walk
-    static constexpr int TOTAL = FBKQ + 8 * DK;
+    // larger trees: the Q rows of one 16-row tile, staged per output tile
+    static constexpr int QT = FBKQ + 8 * DK;
+    static constexpr int TOTAL = QT + (DENSE ? 0 : 16 * KROW);
     static_assert(NMAX * 64 * 4 + DK * 64 * 4 <= NODE, "fallback u and S0 buffers must fit below the node arrays");
 };
 
@@ -391,25 +393,19 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
             }
         };
         if (new_kh && !kq_staged) {
+            if (!DENSE && it != it_begin) prefetch_kq(it, tid, N);
             stage_kq();
             __syncthreads();
         }
-        if (do_gram) {
-            // lower 16x16 tiles holding pairs, dealt round-robin to the
-            // wavefronts; each value lands at its pair (i, s) = path position
-            // dep[s] - 1 of node i
-            int t = 0;
-            for (int I = 0; I < NT; ++I) {
-                const uint32_t tm = tmask[I];
-                for (int J = 0; J <= I; ++J) {
-                    if (!((tm >> J) & 1u)) continue;
-                    if (t++ % NW != wave) continue;
+        // Gram tile (I, J) into the pair list: each value lands at its pair
+        // (i, s) = path position dep[s] - 1 of node i
+        auto gram_tile = [&](int I, int J, const bf16x8 (&qa)[KS]) {
                     f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         const bf16x8 kb = k_frag(16 * J + lc, ks);
                         akk = mfma(k_frag(16 * I + lc, ks), kb, akk);
-                        aqk = mfma(q_frag(16 * I + lc, ks), kb, aqk);
+                        aqk = mfma(qa[ks], kb, aqk);
                     }
                     const int s = 16 * J + lc;
                     const int ds = dep[s];
@@ -429,6 +425,48 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
                             qk[p] = aqk[rr];
                             kk[p] = akk[rr];
                         }
+                    }
+        };
+        if (do_gram) {
+            if constexpr (DENSE) {
+                // lower 16x16 tiles holding pairs, dealt round-robin to the
+                // wavefronts
+                int t = 0;
+                for (int I = 0; I < NT; ++I) {
+                    const uint32_t tm = tmask[I];
+                    bf16x8 qa[KS];
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) qa[ks] = q_frag(16 * I + lc, ks);
+                    for (int J = 0; J <= I; ++J) {
+                        if (!((tm >> J) & 1u)) continue;
+                        if (t++ % NW != wave) continue;
+                        gram_tile(I, J, qa);
+                    }
+                }
+            } else {
+                // Q is not staged: each wavefront takes whole row tiles, whose
+                // Q rows it loads once, the next row tile's while it works on
+                // this one (rows w, 7 - w, 8 + w, 15 - w balance the triangle)
+                static_assert(NW == 4 && NTMAX == 16, "row-tile assignment");
+                auto row_tile = [&](int u) { return (u & 1) ? 8 * (u >> 1) + 7 - wave : 8 * (u >> 1) + wave; };
+                bf16x8 qa[KS], qn[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) qa[ks] = q_frag(16 * row_tile(0) + lc, ks);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int I = row_tile(u);
+                    if (u + 1 < 4) {
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) qn[ks] = q_frag(16 * row_tile(u + 1) + lc, ks);
+                    }
+                    if (I < NT) {
+                        const uint32_t tm = tmask[I];
+                        for (int J = 0; J <= I; ++J)
+                            if ((tm >> J) & 1u) gram_tile(I, J, qa);
+                    }
+                    if (u + 1 < 4) {
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) qa[ks] = qn[ks];
                     }
                 }
             }
@@ -611,7 +649,9 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
             }
         }
         GDN_PHASE(4);
-        if (next_new_kh) prefetch_kq(nit, tid, N);
+        // (larger trees load the next key head's K at the start of its item:
+        // held here, those registers would spill R')
+        if (DENSE && next_new_kh) prefetch_kq(nit, tid, N);
 
         // R' = V - gamma o (K S0^T) as B fragments of the Z~ R' product:
         // k-step kap covers nodes [32 kap, 32 kap + 32); lane (lc, lg) holds
@@ -690,36 +730,68 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
                 }
             }
         } else {
+            // per 16-row tile: its Q rows and its row blocks of Z~ (from the
+            // pair list, in the X area, free after the solve) staged in LDS
+            // by the whole workgroup, then each wavefront's columns
+            unsigned char* Zt = smem + L::XC;
+            unsigned char* Qt = smem + L::QT;
+            auto q_frag_t = [&](int r, int ks) -> bf16x8 { return load_frag(Qt + r * L::KROW + 2 * (8 * KS * lg + 8 * ks)); };
+            // this thread's 16-byte piece of a tile's Q rows, one tile ahead
+            static_assert(16 * (DK / 8) <= NTH, "one Q piece per thread");
+            const int qr = tid / (DK / 8), qc = tid % (DK / 8);
+            auto load_q = [&](int I) {
+                const int row = 16 * I + qr;
+                uint4 val = make_uint4(0u, 0u, 0u, 0u);
+                if (tid < 16 * (DK / 8) && row < N)
+                    val = *reinterpret_cast<const uint4*>(qg + ((static_cast<size_t>(b) * N + row) * Hk + kh) * DK + 8 * qc);
+                return val;
+            };
+            uint4 qv = load_q(0);
             for (int I = 0; I < NT; ++I) {
-                const int irow = 16 * I + lc;
-                f32x4 acc[CT];
-                qs0(I, acc);
-                // this lane's row of Z~, scanned once in node order
-                int p = 0, pend = 0;
-                if (irow < N) {
-                    p = off[irow];
-                    pend = p + dep[irow];
+                const int nb = I / 2 + 1;
+                for (int e = tid; e < nb * 128; e += NTH) reinterpret_cast<uint4*>(Zt)[e] = make_uint4(0u, 0u, 0u, 0u);
+                if (tid < 16 * (DK / 8)) *reinterpret_cast<uint4*>(Qt + qr * L::KROW + 16 * qc) = qv;
+                qv = load_q(min(I + 1, NT - 1));
+                __syncthreads();
+                // the pairs of rows 16 I .. 16 I + 15 are contiguous in the list
+                const int p0 = off[16 * I];
+                const int p1 = 16 * I + 16 < N ? off[16 * I + 16] : total;
+                for (int p = p0 + tid; p < p1; p += NTH) {
+                    const int i = pnode[p], tt = pathc[p];
+                    const float zz = yc[p];
+                    const __bf16 zh = static_cast<__bf16>(zz);
+                    const __bf16 zl = static_cast<__bf16>(zz - static_cast<float>(zh));
+                    const int e = (((((tt >> 2) & 3) << 4) | (i & 15)) << 3) + (((tt >> 4) & 1) << 2) + (tt & 3);
+                    unsigned char* blk = Zt + 2048 * (tt >> 5);
+                    reinterpret_cast<__bf16*>(blk)[e] = zh;
+                    reinterpret_cast<__bf16*>(blk + 1024)[e] = zl;
                 }
+                __syncthreads();
+                f32x4 acc[CT];
+                {
+                    f32x4 ah[CT], al[CT];
+#pragma unroll
+                    for (int st = 0; st < CT; ++st) ah[st] = al[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const bf16x8 qa = q_frag_t(lc, ks);
+#pragma unroll
+                        for (int st = 0; st < CT; ++st) {
+                            ah[st] = mfma(qa, s0h[st][ks], ah[st]);
+                            al[st] = mfma(qa, s0l[st][ks], al[st]);
+                        }
+                    }
+#pragma unroll
+                    for (int st = 0; st < CT; ++st)
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) acc[st][rr] = (ah[st][rr] + al[st][rr]) * gam[16 * I + 4 * lg + rr];
+                }
+                const unsigned char* blk = Zt + 16 * lane;
 #pragma unroll
                 for (int kap = 0; kap < NKMAX; ++kap) {
-                    if (2 * kap > I) continue;
-                    float f[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) f[j] = 0.f;
-                    while (p < pend) {
-                        const int t = pathc[p];
-                        if (t >= 32 * kap + 32) break;
-                        const int dt = t - 32 * kap;
-                        if (((dt >> 2) & 3) == lg) {
-                            const int slot = ((dt >> 4) << 2) | (dt & 3);
-                            const float z = yc[p];
-#pragma unroll
-                            for (int j = 0; j < 8; ++j) f[j] = slot == j ? z : f[j];
-                        }
-                        ++p;
-                    }
-                    bf16x8 zh, zl;
-                    split8(f, zh, zl);
+                    if (kap >= nb) break;
+                    const bf16x8 zh = load_frag(blk + 2048 * kap);
+                    const bf16x8 zl = load_frag(blk + 2048 * kap + 1024);
 #pragma unroll
                     for (int st = 0; st < CT; ++st) {
                         acc[st] = mfma(zh, rh[st][kap], acc[st]);
@@ -728,6 +800,7 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
                     }
                 }
                 store_tile(I, acc);
+                __syncthreads();  // the tile's LDS is rewritten for the next one
             }
         }
         GDN_PHASE(6);
