@@ -109,16 +109,16 @@ struct Lds {
     static_assert(NMAX * 64 * 4 + DK * 64 * 4 <= NODE, "fallback u and S0 buffers must fit below the node arrays");
 };
 
-// Four wavefronts; wavefront w owns CT = d_v / 64 MFMA tiles of 16 value
+// NW wavefronts; wavefront w owns CT = d_v / (16 NW) MFMA tiles of 16 value
 // columns.  With CT = 2 a lane's two columns are adjacent (32 w + 2 lc + st),
 // so V is read in 4-byte and o written in 8-byte pieces.
-template <int NMAX, int DK, int DV>
-__global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int items_per_wg) {
+template <int NMAX, int DK, int DV, int NW>
+__global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int items_per_wg) {
     using L = Lds<NMAX, DK>;
     constexpr bool DENSE = L::DENSE;
-    constexpr int NW = 4;               // wavefronts
     constexpr int NTH = 64 * NW;        // threads
-    constexpr int CT = DV / 64;         // 16-column MFMA tiles per wavefront
+    constexpr int CT = DV / (16 * NW);  // 16-column MFMA tiles per wavefront
+    static_assert(CT == 1 || CT == 2, "one or two column tiles per wavefront");
     constexpr int KS = DK / 32;         // MFMA k-steps over d_k
     constexpr int NTMAX = NMAX / 16;    // 16-row tiles
     constexpr int NKMAX = NMAX / 32;    // 32-node k-steps over the tree
@@ -447,15 +447,17 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
                 // Q is not staged: each wavefront takes whole row tiles, whose
                 // Q rows it loads once, the next row tile's while it works on
                 // this one (rows w, 7 - w, 8 + w, 15 - w balance the triangle)
-                static_assert(NW == 4 && NTMAX == 16, "row-tile assignment");
-                auto row_tile = [&](int u) { return (u & 1) ? 8 * (u >> 1) + 7 - wave : 8 * (u >> 1) + wave; };
+                // (NTMAX / NW row tiles per wavefront, in pairs w, 2 NW - 1 - w)
+                constexpr int RU = NTMAX / NW;
+                static_assert(RU % 2 == 0 && RU * NW == NTMAX, "row-tile assignment");
+                auto row_tile = [&](int u) { return (u & 1) ? 2 * NW * (u >> 1) + 2 * NW - 1 - wave : 2 * NW * (u >> 1) + wave; };
                 bf16x8 qa[KS], qn[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) qa[ks] = q_frag(16 * row_tile(0) + lc, ks);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < RU; ++u) {
                     const int I = row_tile(u);
-                    if (u + 1 < 4) {
+                    if (u + 1 < RU) {
 #pragma unroll
                         for (int ks = 0; ks < KS; ++ks) qn[ks] = q_frag(16 * row_tile(u + 1) + lc, ks);
                     }
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
                         for (int J = 0; J <= I; ++J)
                             if ((tm >> J) & 1u) gram_tile(I, J, qa);
                     }
-                    if (u + 1 < 4) {
+                    if (u + 1 < RU) {
 #pragma unroll
                         for (int ks = 0; ks < KS; ++ks) qa[ks] = qn[ks];
                     }
@@ -819,13 +821,19 @@ __global__ __launch_bounds__(256) void verify_fast_kernel(VerifyArgs a, int item
 }
 
 
+// wavefronts per workgroup: one 16-column tile each (two per SIMD at
+// d_v = 128, which hides more latency than four of two tiles)
+#ifndef GDN_FAST_WAVES
+#define GDN_FAST_WAVES(dk, dv) ((dv) / 16)
+#endif
 template <int NMAX, int DK, int DV>
 hipError_t verify_fast(const VerifyArgs& a, hipStream_t stream) {
+    constexpr int NW = GDN_FAST_WAVES(DK, DV);
     const int items = a.B * a.H_v;
     const int wgs = min(items, device_cus());
     const int per = (items + wgs - 1) / wgs;
     const dim3 grid(static_cast<unsigned>((items + per - 1) / per));
-    hipLaunchKernelGGL((verify_fast_kernel<NMAX, DK, DV>), grid, dim3(256), 0, stream, a, per);
+    hipLaunchKernelGGL((verify_fast_kernel<NMAX, DK, DV, NW>), grid, dim3(64 * NW), 0, stream, a, per);
     return hipGetLastError();
 }
 
