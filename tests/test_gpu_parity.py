@@ -271,6 +271,7 @@ def test_relabelled_tree_permutes_outputs():
     dict(d_k=64, d_v=64), dict(d_k=64, d_v=128), dict(d_k=128, d_v=64), dict(H_k=2, H_v=8),
     dict(N=33, tree="uniform"), dict(dtype="f32", N=70),
     dict(N=64, tree="chain"), dict(N=128, tree="chain"), dict(N=200, tree="uniform"),
+    dict(N=160, d_k=64, d_v=128), dict(N=256, d_k=128, d_v=64, max_depth=24), dict(N=140, d_k=64, d_v=64),
 ])
 def test_edge_shapes(shape):
     base = G.shrink(G.CONFIGS["bestfirst128"], B=2, H_k=2, H_v=4)
@@ -377,6 +378,8 @@ def _mixed_depth_inputs(cfg, seed, chain_every):
     dict(B=40, N=50, H_k=1, H_v=9, d_k=128, d_v=64),
     dict(B=300, N=1, H_k=1, H_v=2),       # single-node trees, 3 heads per workgroup
     dict(B=64, N=17, H_k=2, H_v=8),       # one node past a 16-node tile
+    dict(B=40, N=180, H_k=3, H_v=9),      # trees over 128 nodes, 2 heads per workgroup
+    dict(B=30, N=256, H_k=4, H_v=16, d_k=64, d_v=64),
 ])
 def test_pipeline_item_boundaries(shape, lockstep, monkeypatch):
     """several (sequence, head) items per persistent workgroup: sequence,
