@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--sets", type=int, default=4, help="rotating input sets")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seqs", type=int, default=32, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--no-stress", action="store_true",
+                    help="skip the context figure for one layer of the 48-layer N=256 stress workload")
     ap.add_argument("--kernel-only", action="store_true",
                     help="profiler runs: verify + commit back to back, then the calibration copies; "
                          "prints progress, no JSON")
@@ -336,6 +338,41 @@ def main():
     achieved = vbytes / (verify_ms * 1e-3) / 1e9
     vflops = verify_flops(cfg, float(np.mean([a["mean_strict_ancestors"] for a in anc_depth])))
     traffic = read_traffic("verify")
+    # context (not the metric): one layer of the 48-layer stress workload,
+    # trees of 256 nodes, timed the same way on three rotating layers
+    stress = None
+    first = sets[0]  # the CPU baseline samples it below
+    n_sets = len(sets)
+    if not args.no_stress:
+        del sets
+        torch.cuda.empty_cache()
+        scfg = G.CONFIGS["stress48"]
+        ssets = []
+        for r in range(3):
+            parent = G.make_tree(scfg, G.rng_for(args.seed, 3000 + r))
+            d = G.make_inputs_device(scfg, seed=args.seed, layer=r, parent=parent, device=dev)
+            d["accepted"] = torch.from_numpy(G.rng_for(args.seed, 4000 + r).integers(0, scfg.N, size=scfg.B)
+                                             .astype(np.int32)).to(dev)
+            d["o"] = torch.empty((scfg.B, scfg.N, scfg.H_v, scfg.d_v), dtype=torch.float32, device=dev)
+            d["S_new"] = torch.empty_like(d["S0"])
+            d["ctx"] = gdn.GdnContext.for_tensors(d["q"], d["v"], d["parent"])
+            ssets.append(d)
+        sets = ssets
+        for i in range(6):
+            verify(sets[i % 3])
+            commit(sets[i % 3])
+        torch.cuda.synchronize()
+        sv_ms, sc_ms = timed(verify, 30), timed(commit, 30)
+        for s in sets:
+            gdn.gdn_ctx_status(s["ctx"])
+        sb = verify_bytes(scfg)
+        stress = {"workload": "stress48 layer (B=64, N=256, H_v=32, H_k=16, d=128, depth<=24)",
+                  "verify_us": sv_ms * 1e3, "commit_us": sc_ms * 1e3, "verify_algorithmic_bytes": sb,
+                  "verify_GBps": sb / (sv_ms * 1e-3) / 1e9, "verify_frac_of_peak": sb / (sv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "verify_nodes_heads_per_s": scfg.B * scfg.N * scfg.H_v / (sv_ms * 1e-3)}
+        del ssets, sets
+        torch.cuda.empty_cache()
+
     out = {
         "metric": METRIC,
         "value": nh / (step_ms * 1e-3),
@@ -354,7 +391,7 @@ def main():
                    "tree": f"best_first depth<={cfg.max_depth}",
                    "mean_strict_ancestors": float(np.mean([a["mean_strict_ancestors"] for a in anc_depth])),
                    "max_depth": int(max(a["max_depth"] for a in anc_depth)),
-                   "rotating_sets": len(sets), "step": "gdn_tree_verify + gdn_commit_path",
+                   "rotating_sets": n_sets, "step": "gdn_tree_verify + gdn_commit_path",
                    "arithmetic": "bf16 MFMA with fp32 accumulation; fp32 operands as bf16 hi+lo pairs; "
                                  "fp32 VALU for gates and the triangular solves"},
         "verify": {"ms": verify_ms, "nodes_heads_per_s": nh / (verify_ms * 1e-3),
@@ -370,10 +407,11 @@ def main():
                            "unit": "TFLOP/s", "frac": vflops / (verify_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS},
         "device_copy": {"GBps": copy_gbps, "bytes_per_copy": 2 * (64 << 20) * 4,
                         "note": "torch copy_ of 256 MiB, read + write; context for the 8 TB/s peak"},
+        "context_stress_layer": stress,
         "wall_s_timed_region": wall,
     }
     if args.cpu_seqs > 0:
-        out["cpu_baseline"] = cpu_baseline(sets[0], cfg, args.cpu_seqs)
+        out["cpu_baseline"] = cpu_baseline(first, cfg, args.cpu_seqs)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
