@@ -119,7 +119,11 @@ __global__ __launch_bounds__(512) void verify_grp_kernel(VerifyArgs a, int items
     const int N0 = a.N, Hk = a.H_k, Hv = a.H_v;
     const int R = Hv / Hk;
     const int n_items = a.B * Hv;
-    const int it_begin = blockIdx.x * items_per_wg;
+    // Workgroups go to the 8 XCDs in turn; numbering them so that each XCD
+    // takes consecutive items keeps the heads of a sequence on one XCD, whose
+    // L2 then serves their shared rows of g, beta and the parents once
+    const int wg = gridDim.x % 8 == 0 ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int it_begin = wg * items_per_wg;
     const int it_end = min(it_begin + items_per_wg, n_items);
     if (it_begin >= it_end) return;
 
