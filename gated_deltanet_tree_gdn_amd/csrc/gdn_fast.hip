@@ -33,7 +33,10 @@
 // ancestor pairs (MFMA over the lower 16x16 tiles holding pairs); (4) G,
 // gamma, X, Y, the rows of Z~ (one thread per node) scattered into ready
 // MFMA A fragments; (5) per wavefront: K S0^T -> R', then per 16-row tile
-// Q S0^T and Z~ R' -> o.
+// Q S0^T and Z~ R' -> o (for trees over 128 nodes as the transposed tile,
+// S0 Q^T + R'^T Z~^T, so that each lane stores 16 contiguous bytes of o).
+// Rows of Z~ are solved in registers for paths of up to 16 nodes, or 24
+// for trees over 128 nodes.
 //
 // Trees whose pair list exceeds the LDS budget are verified, inside the same
 // workgroup, by the per-node walk of gdn_walk.h.
@@ -87,7 +90,7 @@ struct Lds {
     static constexpr int KK = ZD + ZD_BYTES;    // float[CAP]: k_i . k_s of every pair (per key head)
     static constexpr int QK = KK + (KEEP_GRAM ? 4 * CAP : 0);  // float[CAP]: q_i . k_s
     static constexpr int XC = QK + (KEEP_GRAM ? 4 * CAP : 0);  // float[CAP]: X (per value head)
-    static constexpr int YC = XC + 4 * (CAP + 16);  // float[CAP]: Y, then the rows of Z~ (X has 16 zero pads)
+    static constexpr int YC = XC + 4 * (CAP + 32);  // float[CAP]: Y, then the rows of Z~ (X has 32 zero pads)
     static constexpr int PATH = YC + 4 * CAP;   // uint8[CAP]: root..i path of every node
     static constexpr int PNODE = PATH + CAP;    // uint8[CAP]: node owning each pair
     static constexpr int NODE = (PNODE + CAP + 15) & ~15;
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
     constexpr int KCH = NMAX * DK / 8 / NTH;  // 16-byte chunks of K (and Q) per thread
     static_assert(KCH >= 1 && NMAX * DK / 8 % NTH == 0, "K staging split");
     constexpr int IPT = (NMAX + NTH - 1) / NTH;  // nodes per thread in node loops
-    constexpr int ZR = 16;              // path length kept in registers when solving a row of Z~
+    constexpr int ZR = NMAX > 128 ? 24 : 16;   // path length kept in registers when solving a row of Z~
 
     __shared__ __align__(16) unsigned char smem[L::TOTAL];
 
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
             xc[p] = x;
             yc[p] = y;
         }
-        if (tid < 16) xc[total + tid] = 0.f;  // pads read by the branch-free solve below
+        if (tid < 32) xc[total + tid] = 0.f;  // pads read by the branch-free solve below
         __syncthreads();
         for (int i = tid; i < N; i += NTH) {
             const int o = off[i], m = dep[i];
@@ -783,14 +786,13 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
                         const bf16x8 qa = q_frag_t(lc, ks);
 #pragma unroll
                         for (int st = 0; st < CT; ++st) {
-                            ah[st] = mfma(qa, s0h[st][ks], ah[st]);
-                            al[st] = mfma(qa, s0l[st][ks], al[st]);
+                            ah[st] = mfma(s0h[st][ks], qa, ah[st]);
+                            al[st] = mfma(s0l[st][ks], qa, al[st]);
                         }
                     }
+                    const float gi = gam[16 * I + lc];
 #pragma unroll
-                    for (int st = 0; st < CT; ++st)
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) acc[st][rr] = (ah[st][rr] + al[st][rr]) * gam[16 * I + 4 * lg + rr];
+                    for (int st = 0; st < CT; ++st) acc[st] = (ah[st] + al[st]) * gi;
                 }
                 const unsigned char* blk = Zt + 16 * lane;
 #pragma unroll
@@ -800,12 +802,22 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
                     const bf16x8 zl = load_frag(blk + 2048 * kap + 1024);
 #pragma unroll
                     for (int st = 0; st < CT; ++st) {
-                        acc[st] = mfma(zh, rh[st][kap], acc[st]);
-                        acc[st] = mfma(zh, rl[st][kap], acc[st]);
-                        acc[st] = mfma(zl, rh[st][kap], acc[st]);
+                        acc[st] = mfma(rh[st][kap], zh, acc[st]);
+                        acc[st] = mfma(rl[st][kap], zh, acc[st]);
+                        acc[st] = mfma(rh[st][kap], zl, acc[st]);
                     }
                 }
-                store_tile(I, acc);
+                // transposed tile: lane (lc, lg) holds value columns
+                // 16 w + 4 lg .. + 3 of node 16 I + lc, one 16-byte store;
+                // o is not read back here
+                {
+                    static_assert(CT == 1, "one 16-column tile per wavefront");
+                    const int i = 16 * I + lc;
+                    if (i < N)
+                        __builtin_nontemporal_store(
+                            acc[0], reinterpret_cast<f32x4*>(a.o + static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV +
+                                                             16 * wave + 4 * lg + static_cast<size_t>(i) * Hv * DV));
+                }
                 __syncthreads();  // the tile's LDS is rewritten for the next one
             }
         }
