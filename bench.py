@@ -194,8 +194,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; --gpus must be 1 "
-              "(sharding is described in DESIGN.md, not run)", file=sys.stderr)
+        print("bench.py: the verify path runs on one GPU; --gpus must be 1 "
+              "(sharding across GPUs is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
