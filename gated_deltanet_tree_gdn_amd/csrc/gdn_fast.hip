@@ -662,7 +662,7 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
         // held here, those registers would spill R')
         if (DENSE && next_new_kh) prefetch_kq(nit, tid, N);
 
-        // R' = V - gamma o (K S0^T) as B fragments of the Z~ R' product:
+        // R' = V - gamma o (K S0^T) as MFMA fragments (k = node) of the Z~ R' product:
         // k-step kap covers nodes [32 kap, 32 kap + 32); lane (lc, lg) holds
         // rows 32 kap + 16 half + 4 lg + rr in slot 4 half + rr.
         bf16x8 rh[CT][NKMAX], rl[CT][NKMAX];
