@@ -26,7 +26,9 @@
 //    scattered into dense MFMA fragments, then per wavefront 16 value
 //    columns: S0 split into bf16 hi + lo, K S0^T -> R', and per 16-node tile
 //    gamma o (S0 Q^T) + R'^T Z~^T (transposed, so a lane stores 16
-//    contiguous bytes).
+//    contiguous bytes).  The two 16-column halves of each 128-byte piece of
+//    an o row belong to the two dense wavefronts of one SIMD, which store
+//    them close together in time, so L2 mostly writes whole lines.
 // The roles meet once per item at a workgroup barrier (twice when K/Q
 // change); inside a role the wavefronts synchronise through an LDS counter
 // (a bounded spin: a fault in the protocol ends the wait instead of hanging
@@ -649,6 +651,9 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
     // identity, which turns it into the layout of K S0^T).
     float4 s0r[CT][2 * KS];
     uint2 vr[CT][NTMAX];
+    // value columns of this wavefront: the two 16-column halves of each
+    // 128-byte row piece of o go to the two dense wavefronts of one SIMD
+    const int colbase = (NWD == 8 && CW == 16) ? 32 * (wave & 3) + 16 * (wave >> 2) : CW * wave;
     // real == 0 (after the last item) keeps the loads, which hold the
     // registers to one value per item, but points every lane at one line
     auto load_sv = [&](int j, int real) {
@@ -656,7 +661,7 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
         const int lcr = lc * real, lgr = lg * real;
 #pragma unroll
         for (int st = 0; st < CT; ++st) {
-            const int c0 = (CW * wave + 16 * st) * real;
+            const int c0 = (colbase + 16 * st) * real;
             const float4* src = reinterpret_cast<const float4*>(
                 a.S0 + ((static_cast<size_t>(bb) * Hv + hh) * DV + c0 + lcr) * DK + 4 * lgr);
 #pragma unroll
@@ -793,7 +798,7 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
         GDN_PHASE(3);
         // O tiles, transposed: O^T = gamma o (S0 Q^T) + R'^T Z~^T; lane
         // (lc, lg) gets value columns CW w + 16 st + 4 lg .. + 3 of node 16 I + lc
-        float* obase = a.o + static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV + CW * wave + 4 * lg;
+        float* obase = a.o + static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV + colbase + 4 * lg;
 #pragma unroll
         for (int I = 0; I < NTMAX; ++I) {
             if (I < NT) {
