@@ -1,9 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark: GDN rollback-free tree verification on one MI355X.
 
-One step = one pass of the whole hot path over one batch: gdn_tree_verify
-(every node's output in one pass, S0 untouched) followed by gdn_commit_path
-(the accepted node's state), on the workload
+The metric is tree-verify throughput: one timed call is gdn_tree_verify
+(every node's output in one pass, S0 untouched) on the workload
 
     best-first proposal trees, depth <= 16, B=32 sequences x N=128 nodes,
     32 value heads sharing 16 key heads, d_k = d_v = 128,
@@ -12,10 +11,11 @@ One step = one pass of the whole hot path over one batch: gdn_tree_verify
 Inputs live in HBM before timing starts; R rotating input sets (>= 3x the
 256 MB Infinity Cache in total) keep the cache from serving the reads.
 
-Prints ONE JSON line.  `value` is nodes*heads per second of the whole step;
-the verify-only rate, the roofline of the dominant kernel (verify, measured
-with HIP events on the stream it runs on) and the fp64 CPU oracle timed on
-this host are reported beside it.
+Prints ONE JSON line.  `value` is nodes*heads per second of gdn_tree_verify
+(B*N*H_v per call over the timed calls).  Beside it: verify followed by
+gdn_commit_path (the accepted node's state) as one step, the roofline of the
+dominant kernel (verify, measured with HIP events on the stream it runs on)
+and the fp64 CPU oracle timed on this host.
 """
 from __future__ import annotations
 
@@ -35,7 +35,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 WORKLOAD = "bestfirst_b32n128"
 KERNEL_SOURCES = ["gdn_tree_api.cpp", "gdn_internal.h", "gdn_mfma.h", "gdn_walk.h", "gdn_simple.hip",
-                  "gdn_fast.hip", "gdn_verify_grp.hip", "gdn_verify_ws.hip", "gdn_commit.hip"]
+                  "gdn_fast.hip", "gdn_verify_ws.hip", "gdn_commit.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_verify_bestfirst_b32n128.json")
 
 
@@ -129,10 +129,20 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(sets0, cfg, max_seqs):
-    """The fp64 oracle, as it stands (the plain per-path replay), on a
-    bounded sample of the same workload: verify and commit of the first
-    `max_seqs` sequences of input set 0."""
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+    except OSError:
+        return "unknown"
+
+
+def cpu_baseline(sets0, cfg, max_seqs, single_seqs=8):
+    """The fp64 oracle as it stands (its memoised form, S_i = step(S_parent),
+    bitwise equal to the per-path replay) on a bounded sample of the same
+    workload: verify and commit of the first `max_seqs` sequences of input
+    set 0 on the oracle's default thread count, then of the first
+    `single_seqs` sequences on one thread."""
     import numpy as np
     import oracle
 
@@ -140,34 +150,35 @@ def cpu_baseline(sets0, cfg, max_seqs):
     host = {n: sets0[n][:nb].float().cpu().numpy().astype(np.float64) for n in ("q", "k", "v", "g", "beta", "S0")}
     host["parent"] = sets0["parent"][:nb].cpu().numpy()
     acc = sets0["accepted"][:nb].cpu().numpy()
-    threads = min(os.cpu_count() or 1, 16)
-    # repeat the sample until about a second of wall time (10-20 s of CPU work)
+    threads = oracle.default_threads()
+    # repeat the sample until about a second of wall time (about 16 s of CPU
+    # work on 16 threads)
     reps, t0 = 0, time.perf_counter()
     while reps < 50 and (reps == 0 or time.perf_counter() - t0 < 1.0):
         oracle.verify_inputs(host, threads=threads)
         oracle.commit_inputs(host, accepted=acc, threads=threads)
         reps += 1
     dt = time.perf_counter() - t0
-    # the same oracle on one thread, over a smaller sample
-    n1 = min(4, nb)
+    n1 = min(single_seqs, nb)
     one = {n: a[:n1] for n, a in host.items()}
     t1 = time.perf_counter()
     oracle.verify_inputs(one, threads=1)
     oracle.commit_inputs(one, accepted=acc[:n1], threads=1)
     dt1 = time.perf_counter() - t1
-    cpu = "unknown"
     try:
-        with open("/proc/cpuinfo") as f:
-            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), cpu)
-    except OSError:
-        pass
-    return {"value": reps * nb * cfg.N * cfg.H_v / dt, "unit": "nodes·heads/s", "cores": threads, "cpu": cpu,
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
+    return {"value": reps * nb * cfg.N * cfg.H_v / dt, "unit": "nodes·heads/s", "cores": threads,
+            "host_logical_cpus": os.cpu_count(), "affinity_cpus": affinity, "cpu": host_cpu_model(),
             "kind": "oracle",
-            "sample": f"fp64 oracle (memoised recurrence, bitwise equal to its per-path replay), verify + "
-                      f"commit of sequences 0..{nb - 1} of input set 0 ({nb}x{cfg.N} nodes x {cfg.H_v} heads), "
-                      f"{reps} repetitions on {threads} threads, {dt:.2f} s wall",
+            "sample": f"fp64 oracle, memoised form (bitwise equal to its per-path replay), verify + commit "
+                      f"of sequences 0..{nb - 1} of input set 0 ({nb}x{cfg.N} nodes x {cfg.H_v} heads), "
+                      f"{reps} repetitions on {threads} threads (OMP_NUM_THREADS or the process's CPUs, "
+                      f"at most {oracle.MAX_THREADS}), {dt:.2f} s wall",
             "single_thread": {"value": n1 * cfg.N * cfg.H_v / dt1, "unit": "nodes·heads/s", "cores": 1,
-                              "sample": f"sequences 0..{n1 - 1}, one repetition, {dt1:.2f} s wall"}}
+                              "sample": f"verify + commit of sequences 0..{n1 - 1}, one repetition, "
+                                        f"{dt1:.2f} s wall"}}
 
 
 def main():
@@ -272,19 +283,21 @@ def main():
     for s in sets:
         gdn.gdn_ctx_status(s["ctx"])
 
-    # --- the timed region: K whole steps --------------------------------------
+    # --- the timed region: K verify calls -------------------------------------
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        s = sets[i % len(sets)]
-        verify(s)
-        commit(s)
+        verify(sets[i % len(sets)])
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = ev0.elapsed_time(ev1) / args.steps
+
+    def step_vc(s):
+        verify(s)
+        commit(s)
 
     # --- per-kernel averages (HIP events on the launch stream) ---------------
     def timed(fn, n):
@@ -297,8 +310,10 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    verify_ms = timed(verify, args.steps)
+    # the timed region is verify alone: its event average is the kernel's
+    verify_ms = step_ms
     commit_ms = timed(commit, args.steps)
+    step_vc_ms = timed(step_vc, args.steps)
 
     # per-call distribution: a HIP event pair around each call
     def per_call(fn, n):
@@ -391,11 +406,13 @@ def main():
                    "tree": f"best_first depth<={cfg.max_depth}",
                    "mean_strict_ancestors": float(np.mean([a["mean_strict_ancestors"] for a in anc_depth])),
                    "max_depth": int(max(a["max_depth"] for a in anc_depth)),
-                   "rotating_sets": n_sets, "step": "gdn_tree_verify + gdn_commit_path",
+                   "rotating_sets": n_sets, "timed_call": "gdn_tree_verify",
                    "arithmetic": "bf16 MFMA with fp32 accumulation; fp32 operands as bf16 hi+lo pairs; "
                                  "fp32 VALU for gates and the triangular solves"},
         "verify": {"ms": verify_ms, "nodes_heads_per_s": nh / (verify_ms * 1e-3),
                    "algorithmic_bytes": vbytes, "GBps": achieved, "per_call": verify_dist},
+        "step_verify_commit": {"ms": step_vc_ms, "nodes_heads_per_s": nh / (step_vc_ms * 1e-3),
+                               "note": "gdn_tree_verify then gdn_commit_path, back to back"},
         "commit": {"ms": commit_ms, "per_call": commit_dist, "algorithmic_bytes": cbytes,
                    "GBps": cbytes / (commit_ms * 1e-3) / 1e9,
                    "frac": cbytes / (commit_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": read_traffic("commit")},

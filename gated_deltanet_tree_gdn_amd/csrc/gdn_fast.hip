@@ -870,11 +870,9 @@ int device_cus() {
 
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     if (a.qkv_dtype != GDN_BF16 || a.force_walk) return launch_verify_simple(a, stream);
-    // trees of up to 128 nodes: one 8-wavefront workgroup per compute unit,
-    // tree and dense parts of consecutive items overlapped on separate
-    // wavefronts (lockstep: the same work in lock step, two heads per tree
-    // pass)
-    if (a.N <= 128) return a.lockstep ? launch_verify_grp(a, stream) : launch_verify_ws(a, stream);
+    // trees of up to 128 nodes: one workgroup per compute unit, tree and
+    // dense parts of consecutive items overlapped on separate wavefronts
+    if (a.N <= 128) return launch_verify_ws(a, stream);
     if (a.d_k == 128) return a.d_v == 128 ? verify_fast<256, 128, 128>(a, stream) : verify_fast<256, 128, 64>(a, stream);
     return a.d_v == 128 ? verify_fast<256, 64, 128>(a, stream) : verify_fast<256, 64, 64>(a, stream);
 }

@@ -28,7 +28,6 @@ struct VerifyArgs {
     float* o;
     int32_t* tree_status;  // [B]: 0 or GDN_ERR_TREE
     int force_walk;        // 1: per-node walk even for bf16 (GDN_FORCE_SIMPLE=1)
-    int lockstep;          // 1: trees of <= 128 nodes by the lock-step kernel (GDN_VERIFY_LOCKSTEP=1)
 };
 
 // Arguments of one accepted-path commit.
@@ -49,8 +48,7 @@ struct CommitArgs {
 
 // Verify dispatch: the MFMA path for bf16 q/k/v, the per-node walk otherwise.
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
-// The MFMA verify for bf16 and N <= 128, two workgroups per compute unit.
-hipError_t launch_verify_grp(const VerifyArgs& a, hipStream_t stream);
+// The MFMA verify for bf16 and N <= 128.
 hipError_t launch_verify_ws(const VerifyArgs& a, hipStream_t stream);
 // Compute units of the current device (cached per device).
 int device_cus();

@@ -23,7 +23,6 @@ struct gdn_ctx {
     int32_t* status;  // device: [B] tree verdicts, then [B] accept verdicts
     bool validate;    // GDN_VALIDATE=1: synchronous host checks of parent/accepted
     bool force_walk;  // GDN_FORCE_SIMPLE=1: per-node walk kernels only
-    bool lockstep;    // GDN_VERIFY_LOCKSTEP=1: lock-step kernel for trees of <= 128 nodes
     bool have_verify;
     bool have_commit;
     const void* k;
@@ -140,8 +139,6 @@ gdn_status gdn_ctx_create(const gdn_tree_dims* dims, void* workspace, size_t wor
     c->validate = env && std::strcmp(env, "1") == 0;
     const char* fw = std::getenv("GDN_FORCE_SIMPLE");
     c->force_walk = fw && std::strcmp(fw, "1") == 0;
-    const char* ls = std::getenv("GDN_VERIFY_LOCKSTEP");
-    c->lockstep = ls && std::strcmp(ls, "1") == 0;
     *out = c;
     return ok();
 }
@@ -173,7 +170,7 @@ gdn_status gdn_tree_verify(gdn_ctx* ctx, const void* q, const void* k, const voi
     GDN_TRY(check_ptr(o, "o"));
     if (ctx->validate) GDN_TRY(host_check_tree(d, parent, stream));
     gdn::VerifyArgs a{d.B, d.N, d.H_k, d.H_v, d.d_k, d.d_v, d.qkv_dtype, q, k, v, g, beta, parent, S0, o,
-                      ctx->status, ctx->force_walk ? 1 : 0, ctx->lockstep ? 1 : 0};
+                      ctx->status, ctx->force_walk ? 1 : 0};
     hipError_t e = gdn::launch_verify(a, stream);
     if (e != hipSuccess) return hip_fail(e, "verify launch");
     ctx->have_verify = true;

@@ -119,7 +119,9 @@ def _one_best_first(rng: np.random.Generator, N: int, max_depth: int) -> np.ndar
     and min(c, N - count) children are appended in rank order (so indices stay
     topological); child r scores score(parent) + log u_(r) with the u's sorted
     in descending order.  If the heap runs dry before N nodes exist, every
-    node below the cap is pushed again.
+    node below the cap that has fewer than 8 children is pushed again; a node
+    expanded a second time receives at most 8 children in all, so no node
+    ever has more than 8.
     """
     ranks = np.arange(1, _ZIPF_RANKS + 1, dtype=np.float64)
     p = ranks ** (-_ZIPF_S)
@@ -129,23 +131,26 @@ def _one_best_first(rng: np.random.Generator, N: int, max_depth: int) -> np.ndar
         return parent
     depth = [1]
     score = [0.0]
+    kids = [0]
     heap = [(-0.0, 0)]
     count = 1
     while count < N:
         if not heap:
-            heap = [(-score[i], i) for i in range(count) if depth[i] < max_depth]
+            heap = [(-score[i], i) for i in range(count) if depth[i] < max_depth and kids[i] < _ZIPF_RANKS]
             heapq.heapify(heap)
             if not heap:
                 raise ValueError("depth cap too small for N nodes")
         _, node = heapq.heappop(heap)
-        if depth[node] >= max_depth:
+        if depth[node] >= max_depth or kids[node] >= _ZIPF_RANKS:
             continue
         c = int(rng.choice(_ZIPF_RANKS, p=p)) + 1
         u = np.sort(rng.random(c))[::-1]
-        m = min(c, N - count)
+        m = min(c, _ZIPF_RANKS - kids[node], N - count)
+        kids[node] += m
         for r in range(m):
             parent[count] = node
             depth.append(depth[node] + 1)
+            kids.append(0)
             score.append(score[node] + float(np.log(u[r])))
             heapq.heappush(heap, (-score[count], count))
             count += 1

@@ -45,9 +45,6 @@
  *  - GDN_FORCE_SIMPLE=1 (read when a context is created) routes that
  *    context's verify to the per-node walk kernels instead of the MFMA path
  *    (for A/B comparison; results agree within the stated tolerance).
- *    GDN_VERIFY_LOCKSTEP=1 (likewise) verifies bf16 trees of up to 128 nodes
- *    with the lock-step MFMA kernel instead of the one that overlaps the tree
- *    and dense parts of consecutive heads (same results up to rounding).
  *  - Calls are asynchronous on `stream` (NULL = the default stream) and
  *    complete in stream order.
  */

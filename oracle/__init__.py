@@ -86,8 +86,25 @@ def _check(rc: int):
         raise OracleError(_ERRORS.get(rc, f"oracle error {rc}"))
 
 
+MAX_THREADS = 16
+
+
+def default_threads() -> int:
+    """Worker threads when none are given: OMP_NUM_THREADS if set, else the
+    CPUs this process may run on, at most MAX_THREADS."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = int(env)
+    else:
+        try:
+            n = len(os.sched_getaffinity(0))
+        except AttributeError:
+            n = os.cpu_count() or 1
+    return max(1, min(n, MAX_THREADS))
+
+
 def _threads(n):
-    return int(n) if n else (os.cpu_count() or 1)
+    return int(n) if n else default_threads()
 
 
 def verify(q, k, v, g, beta, parent, S0, memo: bool = True, threads=None, lib=None) -> np.ndarray:

@@ -84,51 +84,81 @@ def test_parity_workload(name):
     assert_close(S_new.cpu().numpy(), oracle.commit_inputs(inp, accepted=acc), f"{name} S_new")
 
 
-def unit_from_device(d, parent, b, h):
-    """one (sequence, value head) unit of device inputs as fp64 host arrays"""
+def host64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def layer_to_host(d):
+    """every tensor of one device layer as fp64 host arrays (parent int32)"""
+    out = {n: host64(d[n]) for n in ("q", "k", "v", "g", "beta", "S0")}
+    out["parent"] = d["parent"].cpu().numpy()
+    return out
+
+
+def units_to_host(d, units):
+    """the (sequence b, value head h) units of one device layer as a batch of
+    single-head sequences (H_k = H_v = 1), fp64 host arrays"""
     Hk, Hv = d["q"].shape[2], d["v"].shape[2]
-    kh = h // (Hv // Hk)
+    bs = torch.tensor([b for b, _ in units], device=d["q"].device)
+    hs = torch.tensor([h for _, h in units], device=d["q"].device)
+    khs = hs // (Hv // Hk)
+    return {"q": host64(d["q"][bs, :, khs].unsqueeze(2)), "k": host64(d["k"][bs, :, khs].unsqueeze(2)),
+            "v": host64(d["v"][bs, :, hs].unsqueeze(2)), "g": host64(d["g"][bs, :, hs].unsqueeze(2)),
+            "beta": host64(d["beta"][bs, :, hs].unsqueeze(2)), "S0": host64(d["S0"][bs, hs].unsqueeze(1)),
+            "parent": d["parent"][bs].cpu().numpy()}
 
-    def host(t):
-        return t.float().cpu().numpy().astype(np.float64)
 
-    return {"q": host(d["q"][b:b + 1, :, kh:kh + 1]), "k": host(d["k"][b:b + 1, :, kh:kh + 1]),
-            "v": host(d["v"][b:b + 1, :, h:h + 1]), "g": host(d["g"][b:b + 1, :, h:h + 1]),
-            "beta": host(d["beta"][b:b + 1, :, h:h + 1]), "S0": host(d["S0"][b:b + 1, h:h + 1]),
-            "parent": np.ascontiguousarray(parent[b:b + 1])}
+STRESS_UNITS_PER_LAYER = 22   # x 47 layers = 1034 sampled units beyond layer 0
+STRESS_COMMIT_UNITS = 64
 
 
 def test_parity_stress48_sampled():
     """48 layers of B=64, N=256, 32 value / 16 key heads, best-first trees of
-    depth <= 24 shared by all layers: every layer verified on the GPU; all
-    heads of sequence 0 of layer 0 and two seeded (b, h) units of every other
-    layer checked against the oracle; commits sampled on layer 0."""
+    depth <= 24 shared by all layers, every layer verified on the GPU.
+    Checked against the oracle: all 2048 (b, h) units of layer 0 (o and the
+    commit's S_new), and a seeded sample of 22 units in each of layers
+    1..47 (1034 units), plus S_new on 64 seeded units of the last layer."""
     cfg = G.CONFIGS["stress48"]
     parent = G.make_tree(cfg, G.rng_for(0, 0))
     rng = G.rng_for(2)
     ctx = None
+    checked = 0
     for layer in range(cfg.layers):
         d = G.make_inputs_device(cfg, seed=0, layer=layer, parent=parent)
         if ctx is None:
             ctx = gdn.GdnContext.for_tensors(d["q"], d["v"], d["parent"])
         o, _ = run_verify(d, ctx=ctx)
         gdn.gdn_ctx_status(ctx)
-        units = [(0, h) for h in range(cfg.H_v)] if layer == 0 else \
-            [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H_v))) for _ in range(2)]
-        say(f"[parity] stress48 layer {layer}: checking {len(units)} units")
-        got = [o[b, :, h].cpu().numpy() for b, h in units]
-        want = [oracle.verify_inputs(unit_from_device(d, parent, b, h))[0, :, 0] for b, h in units]
-        assert_close(np.stack(got), np.stack(want), f"stress48 layer {layer} sampled o")
         if layer == 0:
+            say(f"[parity] stress48 layer 0: all {cfg.B * cfg.H_v} units")
+            host = layer_to_host(d)
+            assert_close(o.cpu().numpy(), oracle.verify_inputs(host), "stress48 layer 0 o (every unit)")
             acc = rng.integers(-1, cfg.N, size=cfg.B).astype(np.int32)
             S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
             gdn.gdn_ctx_status(ctx)
-            picks = [(0, 0), (0, 17), (5, 31), (int(np.argmax(acc)), 3)]
-            gotS = [S_new[b, h].cpu().numpy() for b, h in picks]
-            wantS = [oracle.commit_inputs(unit_from_device(d, parent, b, h), accepted=acc[b:b + 1])[0, 0]
-                     for b, h in picks]
-            assert_close(np.stack(gotS), np.stack(wantS), "stress48 layer 0 sampled S_new")
+            assert_close(S_new.cpu().numpy(), oracle.commit_inputs(host, accepted=acc),
+                         "stress48 layer 0 S_new (every unit)")
+            checked += cfg.B * cfg.H_v
+            del host, S_new
+        else:
+            units = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H_v))) for _ in range(STRESS_UNITS_PER_LAYER)]
+            say(f"[parity] stress48 layer {layer}: {len(units)} sampled units")
+            got = torch.stack([o[b, :, h] for b, h in units]).unsqueeze(2).cpu().numpy()
+            want = oracle.verify_inputs(units_to_host(d, units))
+            assert_close(got, want, f"stress48 layer {layer} sampled o")
+            checked += len(units)
+        if layer == cfg.layers - 1:
+            units = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H_v))) for _ in range(STRESS_COMMIT_UNITS)]
+            acc = rng.integers(-1, cfg.N, size=cfg.B).astype(np.int32)
+            S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
+            gdn.gdn_ctx_status(ctx)
+            gotS = torch.stack([S_new[b, h] for b, h in units]).unsqueeze(1).cpu().numpy()
+            wantS = oracle.commit_inputs(units_to_host(d, units), accepted=np.array([acc[b] for b, _ in units]))
+            say(f"[parity] stress48 layer {layer}: S_new on {len(units)} sampled units")
+            assert_close(gotS, wantS, f"stress48 layer {layer} sampled S_new")
         del d, o
+    say(f"[parity] stress48: {checked} (layer, b, h) units checked")
+    assert checked >= cfg.B * cfg.H_v + 1024
 
 
 # ----------------------------------------------------------------------------
@@ -187,6 +217,67 @@ def test_ancestors_bit_exact(N):
 # ----------------------------------------------------------------------------
 # properties of rollback-free verification
 # ----------------------------------------------------------------------------
+
+def _repeat_bitwise(fn, calls=10):
+    first = fn().clone()
+    for c in range(1, calls):
+        again = fn()
+        assert torch.equal(first, again), f"call {c} differs from call 0 " \
+            f"({int((first != again).sum())} elements)"
+    return first
+
+
+def test_verify_repeatable_and_prefix_state_untouched_b32n128():
+    """the persistent pipelined verify at B=32, N=128 (several (b, h) items
+    per workgroup, the tree and dense wavefronts handing over through LDS):
+    10 calls bitwise identical; S0 never written"""
+    cfg, inp, d = case_inputs("bestfirst_b32n128")
+    say("[repeat] verify B=32 N=128, 10 calls")
+    S0_before = d["S0"].clone()
+    ctx = gdn.GdnContext.for_tensors(d["q"], d["v"], d["parent"])
+    o = torch.empty((cfg.B, cfg.N, cfg.H_v, cfg.d_v), dtype=torch.float32, device="cuda:0")
+
+    def call():
+        gdn.gdn_tree_verify(ctx, d["q"], d["k"], d["v"], d["g"], d["beta"], d["parent"], d["S0"], o=o)
+        gdn.gdn_ctx_status(ctx)
+        return o
+
+    _repeat_bitwise(call)
+    assert torch.equal(d["S0"], S0_before)
+
+
+def test_verify_repeatable_stress_layer():
+    """one layer of the 256-node stress workload: 10 calls bitwise identical"""
+    cfg = G.CONFIGS["stress48"]
+    parent = G.make_tree(cfg, G.rng_for(0, 0))
+    d = G.make_inputs_device(cfg, seed=0, layer=7, parent=parent)
+    say("[repeat] verify stress layer B=64 N=256, 10 calls")
+    ctx = gdn.GdnContext.for_tensors(d["q"], d["v"], d["parent"])
+    o = torch.empty((cfg.B, cfg.N, cfg.H_v, cfg.d_v), dtype=torch.float32, device="cuda:0")
+
+    def call():
+        gdn.gdn_tree_verify(ctx, d["q"], d["k"], d["v"], d["g"], d["beta"], d["parent"], d["S0"], o=o)
+        gdn.gdn_ctx_status(ctx)
+        return o
+
+    _repeat_bitwise(call)
+
+
+def test_commit_repeatable_b32n128():
+    """the commit at B=32, N=128: 10 calls bitwise identical"""
+    cfg, inp, d = case_inputs("bestfirst_b32n128")
+    acc = torch.from_numpy(G.rng_for(0, 77).integers(-1, cfg.N, size=cfg.B).astype(np.int32)).cuda()
+    _, ctx = run_verify(d)
+    S_new = torch.empty_like(d["S0"])
+    say("[repeat] commit B=32 N=128, 10 calls")
+
+    def call():
+        gdn.gdn_commit_path(ctx, acc, S_new=S_new)
+        gdn.gdn_ctx_status(ctx)
+        return S_new
+
+    _repeat_bitwise(call)
+
 
 def test_prefix_state_untouched_and_deterministic():
     cfg, inp, d = case_inputs("bestfirst128")
@@ -368,7 +459,6 @@ def _mixed_depth_inputs(cfg, seed, chain_every):
     return inp
 
 
-@pytest.mark.parametrize("lockstep", [0, 1])
 @pytest.mark.parametrize("shape", [
     dict(B=40, N=128, H_k=3, H_v=9),      # 2 heads per workgroup, sequence and key-head changes inside one
     dict(B=24, N=64, H_k=4, H_v=16),      # N <= 64 layout, 2 heads per workgroup
@@ -381,15 +471,13 @@ def _mixed_depth_inputs(cfg, seed, chain_every):
     dict(B=40, N=180, H_k=3, H_v=9),      # trees over 128 nodes, 2 heads per workgroup
     dict(B=30, N=256, H_k=4, H_v=16, d_k=64, d_v=64),
 ])
-def test_pipeline_item_boundaries(shape, lockstep, monkeypatch):
+def test_pipeline_item_boundaries(shape):
     """several (sequence, head) items per persistent workgroup: sequence,
     key-head and deep-tree (walk) boundaries between consecutive items"""
-    if lockstep:
-        monkeypatch.setenv("GDN_VERIFY_LOCKSTEP", "1")
     cfg = G.shrink(G.CONFIGS["bestfirst_b32n128"], **shape)
     inp = _mixed_depth_inputs(cfg, seed=11, chain_every=7)
     d = G.to_device(inp)
-    say(f"[pipeline] {shape} lockstep={lockstep}")
+    say(f"[pipeline] {shape}")
     o, ctx = run_verify(d)
     gdn.gdn_ctx_status(ctx)
     assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), f"pipeline {shape} o")
@@ -411,15 +499,12 @@ def _spine_tree(N, k, extra):
     (128, {1: (15, 0), 2: (16, 8), 4: (16, 9), 5: (16, 8)}, {1: 1928, 2: 2048, 4: 2049}),
     (256, {0: (23, 0), 3: (24, 44), 4: (24, 45)}, {0: 5868, 3: 6144, 4: 6145}),
 ])
-@pytest.mark.parametrize("lockstep", [0, 1])
-def test_pair_list_capacity_boundary(N, spines, expect, lockstep, monkeypatch):
+def test_pair_list_capacity_boundary(N, spines, expect):
     """trees whose paths sum to the most a best-first tree of the pages'
     depth reaches (1928 nodes at N = 128, depth 16; 5868 at N = 256, depth
     24), to the pair-list capacity of the MFMA kernels (2048, 6144) and one
     past it, between best-first trees: the first two stay on the MFMA path,
     the last takes the per-node walk"""
-    if lockstep:
-        monkeypatch.setenv("GDN_VERIFY_LOCKSTEP", "1")
     cfg = G.shrink(G.CONFIGS["bestfirst_b32n128"], B=6, N=N, H_k=2, H_v=4)
     inp = G.make_inputs(cfg, seed=5)
     par = inp["parent"].copy()
@@ -429,7 +514,7 @@ def test_pair_list_capacity_boundary(N, spines, expect, lockstep, monkeypatch):
     assert all(totals[b] == t for b, t in expect.items()), totals
     inp["parent"] = par
     d = G.to_device(inp)
-    say(f"[capacity] N={N} path totals {totals} lockstep={lockstep}")
+    say(f"[capacity] N={N} path totals {totals}")
     o, ctx = run_verify(d)
     gdn.gdn_ctx_status(ctx)
     assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), "capacity boundary o")

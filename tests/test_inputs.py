@@ -43,13 +43,22 @@ def test_shapes_and_ranges(name):
         assert np.array_equal(par[0], idx - 1)
 
 
-def test_best_first_branching_and_depth_cap():
+@pytest.mark.parametrize("N,cap", [(256, 24), (128, 16), (60, 3), (73, 3), (200, 4)])
+def test_best_first_branching_and_depth_cap(N, cap):
+    """branching ranks 1..8 and the depth cap hold, also when the heap runs
+    dry and nodes are expanded again (small caps force that: a depth-3 tree
+    holds at most 1 + 8 + 64 = 73 nodes)"""
     rng = G.rng_for(5)
-    par = G.tree_best_first(rng, 8, 256, 24)
+    par = G.tree_best_first(rng, 8, N, cap)
     st = G.tree_stats(par)
-    assert st["max_depth"] <= 24
-    counts = np.bincount(par[par >= 0].ravel())
-    assert counts.max() <= 8 * 4  # a node re-expanded after the heap runs dry may exceed 8
+    assert st["max_depth"] <= cap
+    for p in par:
+        assert np.bincount(p[p >= 0]).max() <= 8
+
+
+def test_best_first_depth_cap_too_small():
+    with pytest.raises(ValueError):
+        G.tree_best_first(G.rng_for(0), 1, 74, 3)
 
 
 def test_bf16_rounding_matches_torch():
