@@ -353,6 +353,40 @@ def main():
     achieved = vbytes / (verify_ms * 1e-3) / 1e9
     vflops = verify_flops(cfg, float(np.mean([a["mean_strict_ancestors"] for a in anc_depth])))
     traffic = read_traffic("verify")
+
+    # the steps around verification, and the per-branch baseline, at the
+    # same workload (context, not the metric)
+    def per_branch(s):
+        gdn.gdn_tree_verify_branches(s["ctx"], s["q"], s["k"], s["v"], s["g"], s["beta"], s["parent"], s["S0"],
+                                     o=s["o"], stream=stream)
+
+    branch_ms = timed(per_branch, 8)
+    for s in sets:
+        gdn.gdn_ctx_status(s["ctx"])
+    rng_t = G.rng_for(args.seed, 5000)
+    root_np, node_np = G.make_candidate_logp(rng_t, cfg.B, cfg.N, 8)
+    root_lp, node_lp = torch.from_numpy(root_np).to(dev), torch.from_numpy(node_np).to(dev)
+    draft_np, target_np = G.make_draft_tokens(sets[0]["parent"].cpu().numpy(), rng_t)
+    draft_t, target_t = torch.from_numpy(draft_np).to(dev), torch.from_numpy(target_np).to(dev)
+    build_w = 8
+    build_out = gdn.gdn_tree_build(root_lp, node_lp, build_w, cfg.max_depth, stream=stream)
+    build_ms = timed(lambda s: gdn.gdn_tree_build(root_lp, node_lp, build_w, cfg.max_depth, stream=stream), 20)
+    acc_out = gdn.gdn_accept_path(sets[0]["parent"], draft_t, target_t, stream=stream)
+    accept_ms = timed(lambda s: gdn.gdn_accept_path(s["parent"], draft_t, target_t, stream=stream), 20)
+    torch.cuda.synchronize()
+    around = {
+        "per_branch_baseline": {
+            "ms": branch_ms, "nodes_heads_per_s": nh / (branch_ms * 1e-3),
+            "fused_speedup": branch_ms / verify_ms, "pages_speedup_at_tree_size_128": 7.1,
+            "note": "gdn_tree_verify_branches: every root-to-leaf branch stepped token by token from a fresh "
+                    "copy of S0 (fp32 VALU); the pages' figure is on other hardware with their own baseline"},
+        "tree_build": {"ms": build_ms, "w": build_w, "candidates": 8, "max_depth": cfg.max_depth,
+                       "steps_max": int(build_out[3].max().item()),
+                       "note": "gdn_tree_build, top-w best-first construction of B=32 trees of N=128 nodes"},
+        "accept_path": {"ms": accept_ms,
+                        "mean_accept_len": float(acc_out[1].float().mean().item()),
+                        "note": "gdn_accept_path, greedy accepted-node selection over B=32 trees of N=128"},
+    }
     # context (not the metric): one layer of the 48-layer stress workload,
     # trees of 256 nodes, timed the same way on three rotating layers
     stress = None
@@ -425,6 +459,7 @@ def main():
         "device_copy": {"GBps": copy_gbps, "bytes_per_copy": 2 * (64 << 20) * 4,
                         "note": "torch copy_ of 256 MiB, read + write; context for the 8 TB/s peak"},
         "context_stress_layer": stress,
+        "around_verify": around,
         "wall_s_timed_region": wall,
     }
     if args.cpu_seqs > 0:

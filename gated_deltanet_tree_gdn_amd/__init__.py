@@ -23,8 +23,8 @@ GDN_BF16, GDN_F32 = 0, 1
 STATUS = ["GDN_OK", "GDN_ERR_NULL", "GDN_ERR_SHAPE", "GDN_ERR_DTYPE", "GDN_ERR_ALIGN",
           "GDN_ERR_WORKSPACE", "GDN_ERR_TREE", "GDN_ERR_ACCEPT", "GDN_ERR_STATE", "GDN_ERR_HIP"]
 EXPORTS = ["gdn_tree_workspace_bytes", "gdn_ctx_create", "gdn_ctx_destroy", "gdn_tree_verify",
-           "gdn_commit_path", "gdn_tree_ancestors", "gdn_ctx_status", "gdn_status_string",
-           "gdn_last_error"]
+           "gdn_tree_verify_branches", "gdn_commit_path", "gdn_tree_ancestors", "gdn_accept_path", "gdn_tree_build", "gdn_ctx_status",
+           "gdn_status_string", "gdn_last_error"]
 
 
 class GdnError(RuntimeError):
@@ -61,10 +61,16 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_ctx_destroy.restype = i32
     lib.gdn_tree_verify.argtypes = [vp] * 10
     lib.gdn_tree_verify.restype = i32
+    lib.gdn_tree_verify_branches.argtypes = [vp] * 10
+    lib.gdn_tree_verify_branches.restype = i32
     lib.gdn_commit_path.argtypes = [vp] * 4
     lib.gdn_commit_path.restype = i32
     lib.gdn_tree_ancestors.argtypes = [dp, vp, vp, vp, vp, vp]
     lib.gdn_tree_ancestors.restype = i32
+    lib.gdn_accept_path.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_accept_path.restype = i32
+    lib.gdn_tree_build.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gdn_tree_build.restype = i32
     lib.gdn_ctx_status.argtypes = [vp, vp]
     lib.gdn_ctx_status.restype = i32
     lib.gdn_status_string.argtypes = [i32]
@@ -177,6 +183,29 @@ def gdn_tree_verify(ctx: GdnContext, q, k, v, g, beta, parent, S0, o=None, strea
     return o
 
 
+def gdn_tree_verify_branches(ctx: GdnContext, q, k, v, g, beta, parent, S0, o=None, stream=None):
+    """The per-branch recurrent baseline: same contract and result as
+    :func:`gdn_tree_verify` (for comparison)."""
+    torch = _torch()
+    d = ctx.dims
+    B, N, Hk, Hv, dk, dv = d.B, d.N, d.H_k, d.H_v, d.d_k, d.d_v
+    qkv = torch.bfloat16 if d.qkv_dtype == GDN_BF16 else torch.float32
+    _require(q, "q", qkv, (B, N, Hk, dk))
+    _require(k, "k", qkv, (B, N, Hk, dk))
+    _require(v, "v", qkv, (B, N, Hv, dv))
+    _require(g, "g", torch.float32, (B, N, Hv))
+    _require(beta, "beta", torch.float32, (B, N, Hv))
+    _require(parent, "parent", torch.int32, (B, N))
+    _require(S0, "S0", torch.float32, (B, Hv, dv, dk))
+    if o is None:
+        o = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=q.device)
+    _require(o, "o", torch.float32, (B, N, Hv, dv))
+    _check(load_library().gdn_tree_verify_branches(ctx.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                                   _ptr(parent), _ptr(S0), _ptr(o), _stream(stream)))
+    ctx._keep = (k, v, g, beta, parent, S0)
+    return o
+
+
 def gdn_commit_path(ctx: GdnContext, accepted, S_new=None, stream=None):
     """S_new[B][H_v][d_v][d_k] (fp32): the state at accepted[b] (S0 where
     accepted[b] == -1), for the tree of the last verify on ``ctx``.
@@ -205,6 +234,46 @@ def gdn_tree_ancestors(parent, stream=None):
     _check(load_library().gdn_tree_ancestors(ctypes.byref(dims), _ptr(parent), _ptr(anc), _ptr(depth),
                                              _ptr(status), _stream(stream)))
     return anc, depth, status[:B]
+
+
+def gdn_accept_path(parent, draft_token, target_token, stream=None):
+    """(accepted [B], accept_len [B], tree_status [B]) int32 device tensors:
+    the greedy accepted node of every sequence, computed on the device."""
+    torch = _torch()
+    _require(parent, "parent", torch.int32)
+    B, N = parent.shape
+    _require(draft_token, "draft_token", torch.int32, (B, N))
+    _require(target_token, "target_token", torch.int32, (B, N + 1))
+    dev = parent.device
+    accepted, accept_len, status = (torch.empty((max(B, 1),), dtype=torch.int32, device=dev) for _ in range(3))
+    dims = Dims(B, N, 1, 1, 64, 64, GDN_BF16)
+    _check(load_library().gdn_accept_path(ctypes.byref(dims), _ptr(parent), _ptr(draft_token),
+                                          _ptr(target_token), _ptr(accepted), _ptr(accept_len), _ptr(status),
+                                          _stream(stream)))
+    return accepted[:B], accept_len[:B], status[:B]
+
+
+def gdn_tree_build(root_logp, node_logp, w, max_depth, stream=None):
+    """(parent, cand_rank, score, steps, build_status) device tensors: the
+    top-w best-first tree of every sequence, built on the device.
+    root_logp [B][C] and node_logp [B][N][C] float32, rows non-increasing."""
+    torch = _torch()
+    _require(root_logp, "root_logp", torch.float32)
+    B, C = root_logp.shape
+    _require(node_logp, "node_logp", torch.float32)
+    N = node_logp.shape[1]
+    _require(node_logp, "node_logp", torch.float32, (B, N, C))
+    dev = root_logp.device
+    parent = torch.empty((B, N), dtype=torch.int32, device=dev)
+    rank = torch.empty((B, N), dtype=torch.int32, device=dev)
+    score = torch.empty((B, N), dtype=torch.float32, device=dev)
+    steps = torch.empty((max(B, 1),), dtype=torch.int32, device=dev)
+    status = torch.empty((max(B, 1),), dtype=torch.int32, device=dev)
+    dims = Dims(B, N, 1, 1, 64, 64, GDN_BF16)
+    _check(load_library().gdn_tree_build(ctypes.byref(dims), int(C), int(w), int(max_depth), _ptr(root_logp),
+                                         _ptr(node_logp), _ptr(parent), _ptr(rank), _ptr(score), _ptr(steps),
+                                         _ptr(status), _stream(stream)))
+    return parent, rank, score, steps[:B], status[:B]
 
 
 def gdn_ctx_status(ctx: GdnContext, stream=None):

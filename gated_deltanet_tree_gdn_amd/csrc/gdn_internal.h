@@ -50,6 +50,8 @@ struct CommitArgs {
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // The MFMA verify for bf16 and N <= 128.
 hipError_t launch_verify_ws(const VerifyArgs& a, hipStream_t stream);
+// Per-branch recurrent verification (the comparison baseline).
+hipError_t launch_verify_branches(const VerifyArgs& a, hipStream_t stream);
 // Compute units of the current device (cached per device).
 int device_cus();
 // The per-node walk for every batch element (any dtype).
@@ -59,5 +61,13 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t stream);
 hipError_t launch_commit_simple(const CommitArgs& a, hipStream_t stream);
 hipError_t launch_ancestors(int B, int N, const int32_t* parent, uint32_t* anc, int32_t* depth,
                             int32_t* tree_status, hipStream_t stream);
+// Greedy accepted-node selection, one wavefront per sequence.
+hipError_t launch_accept(int B, int N, const int32_t* parent, const int32_t* draft, const int32_t* target,
+                         int32_t* accepted, int32_t* accept_len, int32_t* tree_status, hipStream_t stream);
+// Top-w best-first tree construction, one wavefront per sequence (C <= kMaxCand).
+constexpr int kMaxCand = 32;
+hipError_t launch_build(int B, int N, int C, int w, int max_depth, const float* root_logp, const float* node_logp,
+                        int32_t* parent, int32_t* cand_rank, float* score, int32_t* steps, int32_t* build_status,
+                        hipStream_t stream);
 
 }  // namespace gdn

@@ -148,9 +148,13 @@ gdn_status gdn_ctx_destroy(gdn_ctx* ctx) {
     return ok();
 }
 
-gdn_status gdn_tree_verify(gdn_ctx* ctx, const void* q, const void* k, const void* v, const float* g,
-                           const float* beta, const int32_t* parent, const float* S0, float* o,
-                           hipStream_t stream) {
+namespace {
+
+// Shared by both verify entry points: argument checks, the launch, and the
+// record of borrowed inputs for the delayed commit.
+gdn_status verify_with(hipError_t (*launch)(const gdn::VerifyArgs&, hipStream_t), const char* what, gdn_ctx* ctx,
+                       const void* q, const void* k, const void* v, const float* g, const float* beta,
+                       const int32_t* parent, const float* S0, float* o, hipStream_t stream) {
     if (!ctx) return fail(GDN_ERR_NULL, "ctx is NULL");
     const gdn_tree_dims d = ctx->dims;
     ctx->have_verify = false;
@@ -171,11 +175,26 @@ gdn_status gdn_tree_verify(gdn_ctx* ctx, const void* q, const void* k, const voi
     if (ctx->validate) GDN_TRY(host_check_tree(d, parent, stream));
     gdn::VerifyArgs a{d.B, d.N, d.H_k, d.H_v, d.d_k, d.d_v, d.qkv_dtype, q, k, v, g, beta, parent, S0, o,
                       ctx->status, ctx->force_walk ? 1 : 0};
-    hipError_t e = gdn::launch_verify(a, stream);
-    if (e != hipSuccess) return hip_fail(e, "verify launch");
+    hipError_t e = launch(a, stream);
+    if (e != hipSuccess) return hip_fail(e, what);
     ctx->have_verify = true;
     ctx->k = k; ctx->v = v; ctx->g = g; ctx->beta = beta; ctx->parent = parent; ctx->S0 = S0;
     return ok();
+}
+
+}  // namespace
+
+gdn_status gdn_tree_verify(gdn_ctx* ctx, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, const int32_t* parent, const float* S0, float* o,
+                           hipStream_t stream) {
+    return verify_with(gdn::launch_verify, "verify launch", ctx, q, k, v, g, beta, parent, S0, o, stream);
+}
+
+gdn_status gdn_tree_verify_branches(gdn_ctx* ctx, const void* q, const void* k, const void* v, const float* g,
+                                    const float* beta, const int32_t* parent, const float* S0, float* o,
+                                    hipStream_t stream) {
+    return verify_with(gdn::launch_verify_branches, "per-branch verify launch", ctx, q, k, v, g, beta, parent,
+                       S0, o, stream);
 }
 
 gdn_status gdn_commit_path(gdn_ctx* ctx, const int32_t* accepted, float* S_new, hipStream_t stream) {
@@ -211,6 +230,50 @@ gdn_status gdn_tree_ancestors(const gdn_tree_dims* dims, const int32_t* parent, 
     if (tree_status && !aligned16(tree_status)) return fail(GDN_ERR_ALIGN, "tree_status is not 16-byte aligned");
     hipError_t e = gdn::launch_ancestors(dims->B, dims->N, parent, anc, depth, tree_status, stream);
     if (e != hipSuccess) return hip_fail(e, "ancestors launch");
+    return ok();
+}
+
+gdn_status gdn_accept_path(const gdn_tree_dims* dims, const int32_t* parent, const int32_t* draft_token,
+                           const int32_t* target_token, int32_t* accepted, int32_t* accept_len,
+                           int32_t* tree_status, hipStream_t stream) {
+    if (!dims) return fail(GDN_ERR_NULL, "dims is NULL");
+    if (dims->B < 0) return fail(GDN_ERR_SHAPE, "B must be >= 0");
+    if (dims->N < 0 || dims->N > gdn::kMaxN) return fail(GDN_ERR_SHAPE, "N must be in [0, 256]");
+    if (dims->B == 0) return ok();
+    GDN_TRY(check_ptr(accepted, "accepted"));
+    GDN_TRY(check_ptr(target_token, "target_token"));
+    if (dims->N > 0) {
+        GDN_TRY(check_ptr(parent, "parent"));
+        GDN_TRY(check_ptr(draft_token, "draft_token"));
+    }
+    if (accept_len && !aligned16(accept_len)) return fail(GDN_ERR_ALIGN, "accept_len is not 16-byte aligned");
+    if (tree_status && !aligned16(tree_status)) return fail(GDN_ERR_ALIGN, "tree_status is not 16-byte aligned");
+    hipError_t e = gdn::launch_accept(dims->B, dims->N, parent, draft_token, target_token, accepted, accept_len,
+                                      tree_status, stream);
+    if (e != hipSuccess) return hip_fail(e, "accept launch");
+    return ok();
+}
+
+gdn_status gdn_tree_build(const gdn_tree_dims* dims, int32_t n_cand, int32_t w, int32_t max_depth,
+                          const float* root_logp, const float* node_logp, int32_t* parent, int32_t* cand_rank,
+                          float* score, int32_t* steps, int32_t* build_status, hipStream_t stream) {
+    if (!dims) return fail(GDN_ERR_NULL, "dims is NULL");
+    if (dims->B < 0) return fail(GDN_ERR_SHAPE, "B must be >= 0");
+    if (dims->N < 0 || dims->N > gdn::kMaxN) return fail(GDN_ERR_SHAPE, "N must be in [0, 256]");
+    if (n_cand < 1 || n_cand > gdn::kMaxCand) return fail(GDN_ERR_SHAPE, "n_cand must be in [1, 32]");
+    if (w < 1) return fail(GDN_ERR_SHAPE, "w must be >= 1");
+    if (max_depth < 1) return fail(GDN_ERR_SHAPE, "max_depth must be >= 1");
+    if (dims->B == 0 || dims->N == 0) return ok();
+    GDN_TRY(check_ptr(root_logp, "root_logp"));
+    GDN_TRY(check_ptr(node_logp, "node_logp"));
+    GDN_TRY(check_ptr(parent, "parent"));
+    if (cand_rank && !aligned16(cand_rank)) return fail(GDN_ERR_ALIGN, "cand_rank is not 16-byte aligned");
+    if (score && !aligned16(score)) return fail(GDN_ERR_ALIGN, "score is not 16-byte aligned");
+    if (steps && !aligned16(steps)) return fail(GDN_ERR_ALIGN, "steps is not 16-byte aligned");
+    if (build_status && !aligned16(build_status)) return fail(GDN_ERR_ALIGN, "build_status is not 16-byte aligned");
+    hipError_t e = gdn::launch_build(dims->B, dims->N, n_cand, w, max_depth, root_logp, node_logp, parent,
+                                     cand_rank, score, steps, build_status, stream);
+    if (e != hipSuccess) return hip_fail(e, "tree-build launch");
     return ok();
 }
 

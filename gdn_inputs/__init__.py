@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "Config", "CONFIGS", "rng_for", "tree_uniform", "tree_chain", "tree_best_first",
     "round_bf16_bits", "bf16_bits_to_f32", "make_inputs", "make_inputs_device", "tree_stats",
-    "to_device", "shrink",
+    "to_device", "shrink", "make_draft_tokens", "make_candidate_logp",
 ]
 
 
@@ -315,3 +315,53 @@ def to_device(inp: dict, device="cuda") -> dict:
     if "accepted" in inp:
         out["accepted"] = torch.from_numpy(np.ascontiguousarray(inp["accepted"], dtype=np.int32)).to(device)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Tokens and candidate scores for the steps around verification
+# ----------------------------------------------------------------------------
+
+def make_draft_tokens(parent: np.ndarray, rng: np.random.Generator, vocab: int = 32000,
+                      p_match: float = 0.8):
+    """Synthetic drafted tokens and verifier choices for a batch of trees.
+
+    draft_token [B][N]: each node's token; the children of one node draw
+    distinct tokens (a drafter proposes distinct continuations).
+    target_token [B][N+1]: the verifier's choice after the prefix (index 0)
+    and after node i (index i + 1).  With probability p_match it is the token
+    of one of that context's children, the k-th child (in index order) picked
+    with weight 1 / (k + 1); otherwise a token none of the children drafted.
+    """
+    parent = np.asarray(parent)
+    B, N = parent.shape
+    draft = np.zeros((B, N), dtype=np.int32)
+    target = np.zeros((B, N + 1), dtype=np.int32)
+    for b in range(B):
+        kids = {c: [] for c in range(-1, N)}
+        for i in range(N):
+            kids[int(parent[b, i])].append(i)
+        for c, ch in kids.items():
+            if ch:
+                draft[b, ch] = rng.choice(vocab, size=len(ch), replace=False)
+        for c, ch in kids.items():
+            if ch and rng.random() < p_match:
+                wts = 1.0 / np.arange(1, len(ch) + 1)
+                target[b, c + 1] = draft[b, ch[int(rng.choice(len(ch), p=wts / wts.sum()))]]
+            else:
+                taken = set(int(draft[b, i]) for i in ch)
+                t = int(rng.integers(vocab))
+                while t in taken:
+                    t = int(rng.integers(vocab))
+                target[b, c + 1] = t
+    return draft, target
+
+
+def make_candidate_logp(rng: np.random.Generator, B: int, N: int, C: int = 8, alpha: float = 0.3):
+    """Synthetic drafter scores for tree construction: root_logp [B][C] and
+    node_logp [B][N][C], each row the log of a Dirichlet(alpha) draw over C
+    candidates sorted best first (fp32; probabilities below 1e-30 are clipped
+    so every log-probability is finite)."""
+    p = rng.dirichlet(np.full(C, alpha), size=(B, N + 1))
+    p = -np.sort(-p, axis=-1)
+    logp = np.log(np.maximum(p, 1e-30)).astype(np.float32)
+    return np.ascontiguousarray(logp[:, 0]), np.ascontiguousarray(logp[:, 1:])

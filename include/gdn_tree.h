@@ -120,6 +120,18 @@ gdn_status gdn_tree_verify(gdn_ctx* ctx, const void* q, const void* k, const voi
                            const float* g, const float* beta, const int32_t* parent,
                            const float* S0, float* o, hipStream_t stream);
 
+/* Per-branch recurrent verification, the baseline the fused verification is
+ * compared with (Trees from Marginals technical summary, Experimental
+ * Results: 7.1x at tree size 128; wispaper.ai page, "Systems Innovation:
+ * Fused GDN Verification").  Same arguments, outputs, context record and
+ * status as gdn_tree_verify; each root-to-leaf branch is run as its own
+ * sequence from a fresh copy of S0, token by token, so nodes shared by
+ * several branches are recomputed once per branch.  Results equal
+ * gdn_tree_verify's up to rounding.  Far slower; for comparison only. */
+gdn_status gdn_tree_verify_branches(gdn_ctx* ctx, const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta, const int32_t* parent,
+                                    const float* S0, float* o, hipStream_t stream);
+
 /* Delayed state commitment for the accepted node (same section): for each
  * sequence b, S_new[b] is the state the recurrence reaches at accepted[b]
  * when run from S0 along the root-to-accepted path of the tree recorded by
@@ -142,6 +154,58 @@ gdn_status gdn_commit_path(gdn_ctx* ctx, const int32_t* accepted, float* S_new,
  * Only B and N of dims are used.  Asynchronous on stream. */
 gdn_status gdn_tree_ancestors(const gdn_tree_dims* dims, const int32_t* parent, uint32_t* anc,
                               int32_t* depth, int32_t* tree_status, hipStream_t stream);
+
+/* Accepted-node selection: the step between a verify and the delayed
+ * commit, which commits the state once the accepted branch is known (same
+ * section).  The pages do not print the acceptance rule; this is greedy
+ * matching from the root, the rule of lossless greedy speculative decoding:
+ * starting at the prefix, move to the lowest-index child whose drafted token
+ * equals the verifier's choice after the current node, until no child
+ * matches.  accepted[b] is the last node reached (-1 if none) and can be
+ * passed straight to gdn_commit_path; accept_len[b] is its depth, the number
+ * of drafted tokens accepted.
+ *   parent       [B][N]   int32, topological (an invalid entry is flagged
+ *                         and read as -1)
+ *   draft_token  [B][N]   int32, the token each node drafts
+ *   target_token [B][N+1] int32, the verifier's choice after the prefix
+ *                         (index 0) and after each node i (index i + 1)
+ *   accepted     [B]      int32, written
+ *   accept_len   [B]      int32, written; may be NULL
+ *   tree_status  [B]      int32, written: 0 or GDN_ERR_TREE; may be NULL
+ * Only B and N of dims are used; N == 0 gives accepted = -1.  Asynchronous
+ * on stream. */
+gdn_status gdn_accept_path(const gdn_tree_dims* dims, const int32_t* parent, const int32_t* draft_token,
+                           const int32_t* target_token, int32_t* accepted, int32_t* accept_len,
+                           int32_t* tree_status, hipStream_t stream);
+
+/* Draft-tree construction upstream of verification (Trees from Marginals,
+ * technical summary, Methodology, "2. Tree Construction"): a best-first
+ * search over candidate continuations that pops the w best candidates of
+ * the heap at a time and expands them together, so N nodes take about
+ * ceil(N / w) sequential steps.  Candidate r of the prefix scores
+ * root_logp[b][r]; once node j exists, its candidate r scores
+ * score[j] + node_logp[b][j][r] (fp32).  Ties go to the lower parent (the
+ * prefix first), then to the lower rank.  The popped candidates become nodes
+ * in pop order, so the parent array is topological; a step's nodes are
+ * expanded only when the step ends, and a node at depth max_depth (the
+ * prefix's children have depth 1) is not expanded.
+ *   root_logp  [B][n_cand]     fp32, each row non-increasing (best first)
+ *   node_logp  [B][N][n_cand]  fp32, row j = candidates of the node that
+ *                              becomes node j; each row non-increasing
+ *   parent     [B][N]          int32, written
+ *   cand_rank  [B][N]          int32, written: each node's rank among its
+ *                              parent's candidates; may be NULL
+ *   score      [B][N]          fp32, written: each node's score; may be NULL
+ *   steps      [B]             int32, written: expansion steps taken; may be NULL
+ *   build_status [B]           int32, written: 0, GDN_ERR_SHAPE (a row is
+ *                              not non-increasing), or GDN_ERR_TREE (the heap
+ *                              ran dry before N nodes); outputs of such a
+ *                              sequence are unspecified; may be NULL
+ * n_cand in [1, 32], w >= 1, max_depth >= 1; log-probabilities must be
+ * finite.  Only B and N of dims are used.  Asynchronous on stream. */
+gdn_status gdn_tree_build(const gdn_tree_dims* dims, int32_t n_cand, int32_t w, int32_t max_depth,
+                          const float* root_logp, const float* node_logp, int32_t* parent, int32_t* cand_rank,
+                          float* score, int32_t* steps, int32_t* build_status, hipStream_t stream);
 
 /* Synchronises `stream` and reports the device-side verdicts of the last
  * verify (GDN_ERR_TREE if any sequence had an invalid parent array;

@@ -173,6 +173,35 @@ int main() {
     CHECK(gdn_tree_ancestors(&d, t.parent, reinterpret_cast<uint32_t*>(t.o), t.accepted, nullptr, nullptr) == GDN_OK);
     CHECK(g_stub.ancestors == 1);
 
+    // per-branch verify: same checks, and it arms the commit
+    CHECK(gdn_ctx_create(&d, work, ws, &c) == GDN_OK);
+    CHECK(gdn_tree_verify_branches(c, t.q, t.k, nullptr, t.g, t.beta, t.parent, t.S0, t.o, nullptr) == GDN_ERR_NULL);
+    CHECK(gdn_commit_path(c, t.accepted, t.S_new, nullptr) == GDN_ERR_STATE);
+    CHECK(gdn_tree_verify_branches(c, t.q, t.k, t.v, t.g, t.beta, t.parent, t.S0, t.o, nullptr) == GDN_OK);
+    CHECK(g_stub.branch_verifies == 1 && g_stub.last_verify.v == t.v);
+    CHECK(gdn_commit_path(c, t.accepted, t.S_new, nullptr) == GDN_OK);
+    CHECK(gdn_ctx_destroy(c) == GDN_OK);
+
+    // accepted-node selection and tree construction
+    int32_t* target = static_cast<int32_t*>(dev_alloc(static_cast<size_t>(d.B) * (d.N + 1) * 4));
+    int32_t* lens = static_cast<int32_t*>(dev_alloc(d.B * 4));
+    CHECK(gdn_accept_path(&d, t.parent, t.parent, target, t.accepted, lens, nullptr, nullptr) == GDN_OK);
+    CHECK(g_stub.accepts == 1 && t.accepted[0] == -1);
+    CHECK(gdn_accept_path(&d, t.parent, nullptr, target, t.accepted, lens, nullptr, nullptr) == GDN_ERR_NULL);
+    CHECK(gdn_accept_path(&d, t.parent, t.parent, target, t.accepted, lens + 1, nullptr, nullptr) == GDN_ERR_ALIGN);
+    float* root = static_cast<float*>(dev_alloc(static_cast<size_t>(d.B) * 8 * 4));
+    float* node = static_cast<float*>(dev_alloc(static_cast<size_t>(d.B) * d.N * 8 * 4));
+    CHECK(gdn_tree_build(&d, 8, 4, 16, root, node, t.parent, reinterpret_cast<int32_t*>(t.o) + 1, nullptr, nullptr,
+                         nullptr, nullptr) == GDN_ERR_ALIGN);
+    CHECK(gdn_tree_build(&d, 0, 4, 16, root, node, t.parent, nullptr, nullptr, nullptr, nullptr, nullptr) ==
+          GDN_ERR_SHAPE);
+    CHECK(gdn_tree_build(&d, 8, 4, 16, root, node, t.parent, nullptr, nullptr, lens, nullptr, nullptr) == GDN_OK);
+    CHECK(g_stub.builds == 1 && lens[0] == 1 && t.parent[0] == -1);
+    std::free(target);
+    std::free(lens);
+    std::free(root);
+    std::free(node);
+
     // status names
     for (int s = 0; s <= GDN_ERR_HIP; ++s) CHECK(std::strncmp(gdn_status_string(static_cast<gdn_status>(s)), "GDN_", 4) == 0);
     CHECK(std::strcmp(gdn_status_string(static_cast<gdn_status>(99)), "GDN_ERR_UNKNOWN") == 0);

@@ -45,6 +45,39 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t) {
     return g_stub.launch_error;
 }
 
+hipError_t launch_verify_branches(const VerifyArgs& a, hipStream_t) {
+    ++g_stub.branch_verifies;
+    g_stub.last_verify = a;
+    for (int b = 0; b < a.B; ++b) a.tree_status[b] = g_stub.verify_verdict;
+    return g_stub.launch_error;
+}
+
+hipError_t launch_accept(int B, int, const int32_t*, const int32_t*, const int32_t*, int32_t* accepted,
+                         int32_t* accept_len, int32_t* tree_status, hipStream_t) {
+    ++g_stub.accepts;
+    for (int b = 0; b < B; ++b) {
+        accepted[b] = -1;
+        if (accept_len) accept_len[b] = 0;
+        if (tree_status) tree_status[b] = 0;
+    }
+    return g_stub.launch_error;
+}
+
+hipError_t launch_build(int B, int N, int, int, int, const float*, const float*, int32_t* parent, int32_t* cand_rank,
+                        float* score, int32_t* steps, int32_t* build_status, hipStream_t) {
+    ++g_stub.builds;
+    for (int i = 0; i < B * N; ++i) {
+        parent[i] = -1;
+        if (cand_rank) cand_rank[i] = 0;
+        if (score) score[i] = 0.f;
+    }
+    for (int b = 0; b < B; ++b) {
+        if (steps) steps[b] = 1;
+        if (build_status) build_status[b] = 0;
+    }
+    return g_stub.launch_error;
+}
+
 hipError_t launch_ancestors(int B, int N, const int32_t*, uint32_t*, int32_t*, int32_t* tree_status, hipStream_t) {
     ++g_stub.ancestors;
     if (tree_status)

@@ -142,3 +142,33 @@ def test_python_binding_has_no_cpu_fallback():
     src = open(os.path.join(ROOT, "gated_deltanet_tree_gdn_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("oracle is", "")
     assert "numpy" not in src
+
+
+def test_accept_path_arg_checks(lib):
+    d = dims(N=300)
+    assert gdn.STATUS[lib.gdn_accept_path(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None)] == "GDN_ERR_SHAPE"
+    d = dims()
+    assert gdn.STATUS[lib.gdn_accept_path(None, FAKE, FAKE, FAKE, FAKE, None, None, None)] == "GDN_ERR_NULL"
+    for i in range(4):
+        args = [FAKE] * 4
+        args[i] = None
+        assert gdn.STATUS[lib.gdn_accept_path(ctypes.byref(d), *args, None, None, None)] == "GDN_ERR_NULL"
+        args[i] = FAKE + 4
+        assert gdn.STATUS[lib.gdn_accept_path(ctypes.byref(d), *args, None, None, None)] == "GDN_ERR_ALIGN"
+    assert gdn.STATUS[lib.gdn_accept_path(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE + 8, None, None)] == "GDN_ERR_ALIGN"
+    assert lib.gdn_accept_path(ctypes.byref(dims(B=0)), None, None, None, None, None, None, None) == 0
+
+
+def test_tree_build_arg_checks(lib):
+    d = dims()
+    ok = (8, 4, 16, FAKE, FAKE, FAKE, None, None, None, None, None)
+    for bad in ((0,) + ok[1:], (33,) + ok[1:], ok[:1] + (0,) + ok[2:], ok[:2] + (0,) + ok[3:]):
+        assert gdn.STATUS[lib.gdn_tree_build(ctypes.byref(d), *bad)] == "GDN_ERR_SHAPE"
+    assert gdn.STATUS[lib.gdn_tree_build(ctypes.byref(dims(N=257)), *ok)] == "GDN_ERR_SHAPE"
+    for i in (3, 4, 5):
+        args = list(ok)
+        args[i] = None
+        assert gdn.STATUS[lib.gdn_tree_build(ctypes.byref(d), *args)] == "GDN_ERR_NULL"
+        args[i] = FAKE + 4
+        assert gdn.STATUS[lib.gdn_tree_build(ctypes.byref(d), *args)] == "GDN_ERR_ALIGN"
+    assert lib.gdn_tree_build(ctypes.byref(dims(N=0)), *ok) == 0
