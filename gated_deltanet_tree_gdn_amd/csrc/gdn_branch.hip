@@ -99,20 +99,42 @@ __global__ __launch_bounds__(DV) void branch_kernel(VerifyArgs a, int splits) {
             S[j + 2] = x.z;
             S[j + 3] = x.w;
         }
-        // root first: path[m-1] .. path[0]
-        for (int t = m - 1; t >= 0; --t) {
+        // root first: path[m-1] .. path[0]; the next node's inputs are
+        // loaded while the current one is applied
+        constexpr int KPT = (DK + DV - 1) / DV;   // k / q elements per thread
+        float pk[KPT], pq[KPT], pg = 0.f, pb = 0.f, pv = 0.f;
+        auto prefetch = [&](int t) {
             const int i = path[t];
             const size_t nk = ((static_cast<size_t>(b) * N + i) * Hk + kh) * DK;
-            __syncthreads();   // the previous step's k, q are read
-            for (int j = c; j < DK; j += DV) {
-                kv[j] = ld(kg + nk + j);
-                qv[j] = ld(qg + nk + j);
-            }
-            __syncthreads();
             const size_t nh = (static_cast<size_t>(b) * N + i) * Hv + h;
-            const float alpha = __expf(a.g[nh]);
-            const float beta = a.beta[nh];
-            const float vc = ld(vg + nh * DV + c);
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const int j = c + e * DV;
+                pk[e] = j < DK ? ld(kg + nk + j) : 0.f;
+                pq[e] = j < DK ? ld(qg + nk + j) : 0.f;
+            }
+            pg = a.g[nh];
+            pb = a.beta[nh];
+            pv = ld(vg + nh * DV + c);
+        };
+        if (m > 0) prefetch(m - 1);
+        for (int t = m - 1; t >= 0; --t) {
+            const int i = path[t];
+            const size_t nh = (static_cast<size_t>(b) * N + i) * Hv + h;
+            __syncthreads();   // the previous step's k, q are read
+#pragma unroll
+            for (int e = 0; e < KPT; ++e) {
+                const int j = c + e * DV;
+                if (j < DK) {
+                    kv[j] = pk[e];
+                    qv[j] = pq[e];
+                }
+            }
+            const float alpha = __expf(pg);
+            const float beta = pb;
+            const float vc = pv;
+            __syncthreads();
+            if (t > 0) prefetch(t - 1);
             float sk = 0.f;
 #pragma unroll
             for (int j = 0; j < DK; ++j) sk += S[j] * kv[j];

@@ -85,6 +85,28 @@ __global__ __launch_bounds__(64) void accept_kernel(int N, const int32_t* __rest
 // within a position the list order is the rank order), after which that
 // position's head moves on.  A step pops up to w heads; the nodes it places
 // get their own heads only when the step ends.
+// Wave-wide max / min with DPP row operations (pairs, quads, half rows,
+// rows, then the row broadcasts 15 and 31); the result is read from lane 63
+// and returned to every lane.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+    int x = static_cast<int>(v);
+    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false))));
+    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false))));
+    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false))));
+    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false))));
+    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false))));
+    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false))));
+    return static_cast<T>(__builtin_amdgcn_readlane(x, 63));
+}
+
+struct MaxU {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
+};
+struct MinI {
+    __device__ int operator()(int a, int b) const { return a < b ? a : b; }
+};
+
 __device__ __forceinline__ uint32_t orderable(float x) {
     const uint32_t u = __float_as_uint(x);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -135,8 +157,7 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
             uint32_t key = 0u;
 #pragma unroll
             for (int e = 0; e < kU; ++e) key = max(key, hs[e] == NEG ? 0u : orderable(hs[e]));
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) key = max(key, static_cast<uint32_t>(__shfl_xor(static_cast<int>(key), o, 64)));
+            key = wave_reduce<uint32_t>(key, MaxU{});
             if (key == 0u) break;   // every list is spent
             // lowest position among the lanes holding that key (a lane's own
             // best position is its lowest one with that key)
@@ -144,8 +165,7 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
 #pragma unroll
             for (int e = 0; e < kU; ++e)
                 if (hs[e] != NEG && orderable(hs[e]) == key) cand = min(cand, l + 64 * e);
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) cand = min(cand, __shfl_xor(cand, o, 64));
+            cand = wave_reduce<int>(cand, MinI{});
             const int u = cand, owner = u & 63, eo = u >> 6;
             if (l == owner) {
 #pragma unroll

@@ -50,6 +50,9 @@ struct CommitArgs {
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // The MFMA verify for bf16 and N <= 128.
 hipError_t launch_verify_ws(const VerifyArgs& a, hipStream_t stream);
+// Item-per-workgroup MFMA verify (bf16, N <= 128); not dispatched by
+// launch_verify, kept for the fused commit-then-verify path.
+hipError_t launch_verify_item(const VerifyArgs& a, hipStream_t stream);
 // Per-branch recurrent verification (the comparison baseline).
 hipError_t launch_verify_branches(const VerifyArgs& a, hipStream_t stream);
 // Compute units of the current device (cached per device).
