@@ -23,7 +23,7 @@ GDN_BF16, GDN_F32 = 0, 1
 STATUS = ["GDN_OK", "GDN_ERR_NULL", "GDN_ERR_SHAPE", "GDN_ERR_DTYPE", "GDN_ERR_ALIGN",
           "GDN_ERR_WORKSPACE", "GDN_ERR_TREE", "GDN_ERR_ACCEPT", "GDN_ERR_STATE", "GDN_ERR_HIP"]
 EXPORTS = ["gdn_tree_workspace_bytes", "gdn_ctx_create", "gdn_ctx_destroy", "gdn_tree_verify",
-           "gdn_tree_verify_branches", "gdn_commit_path", "gdn_tree_ancestors", "gdn_accept_path", "gdn_tree_build", "gdn_ctx_status",
+           "gdn_tree_verify_branches", "gdn_commit_path", "gdn_tree_ancestors", "gdn_accept_path", "gdn_tree_build", "gdn_tree_verify_static", "gdn_ctx_status",
            "gdn_status_string", "gdn_last_error"]
 
 
@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_accept_path.restype = i32
     lib.gdn_tree_build.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_tree_build.restype = i32
+    lib.gdn_tree_verify_static.argtypes = [dp] + [vp] * 9
+    lib.gdn_tree_verify_static.restype = i32
     lib.gdn_ctx_status.argtypes = [vp, vp]
     lib.gdn_ctx_status.restype = i32
     lib.gdn_status_string.argtypes = [i32]
@@ -274,6 +276,25 @@ def gdn_tree_build(root_logp, node_logp, w, max_depth, stream=None):
                                          _ptr(node_logp), _ptr(parent), _ptr(rank), _ptr(score), _ptr(steps),
                                          _ptr(status), _stream(stream)))
     return parent, rank, score, steps[:B], status[:B]
+
+
+def gdn_tree_verify_static(q, k, v, g, beta, parent, S0, o=None, stream=None):
+    """:func:`gdn_tree_verify` for callers that cannot allocate device memory:
+    no context, no workspace (the library's fixed device array takes the
+    per-sequence verdicts).  ``o`` must be passed in to allocate nothing."""
+    torch = _torch()
+    B, N, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    code = _dtype_code(q)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (g, "g"), (beta, "beta"), (parent, "parent"), (S0, "S0")):
+        _require(t, name)
+    if o is None:
+        o = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=q.device)
+    _require(o, "o", torch.float32, (B, N, Hv, dv))
+    dims = Dims(B, N, Hk, Hv, dk, dv, code)
+    _check(load_library().gdn_tree_verify_static(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                                 _ptr(beta), _ptr(parent), _ptr(S0), _ptr(o), _stream(stream)))
+    return o
 
 
 def gdn_ctx_status(ctx: GdnContext, stream=None):

@@ -6,6 +6,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <string>
 
 #include "gdn_tree.h"
 
@@ -55,6 +56,8 @@ hipError_t launch_verify_ws(const VerifyArgs& a, hipStream_t stream);
 hipError_t launch_verify_item(const VerifyArgs& a, hipStream_t stream);
 // Per-branch recurrent verification (the comparison baseline).
 hipError_t launch_verify_branches(const VerifyArgs& a, hipStream_t stream);
+// Sets the calling thread's detail message (gdn_last_error).
+void set_last_error(const std::string& msg);
 // Compute units of the current device (cached per device).
 int device_cus();
 // The per-node walk for every batch element (any dtype).

@@ -114,6 +114,10 @@ gdn_status host_check_accepted(const gdn_tree_dims& d, const int32_t* accepted, 
 
 }  // namespace
 
+namespace gdn {
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+}  // namespace gdn
+
 extern "C" {
 
 size_t gdn_tree_workspace_bytes(const gdn_tree_dims* dims) {

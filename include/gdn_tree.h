@@ -215,6 +215,23 @@ gdn_status gdn_tree_build(const gdn_tree_dims* dims, int32_t n_cand, int32_t w, 
  * GDN_OK otherwise. */
 gdn_status gdn_ctx_status(gdn_ctx* ctx, hipStream_t stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation:
+ * gdn_tree_verify without a context or a caller workspace.  Same inputs,
+ * output and kernels as gdn_tree_verify; the per-sequence verdicts those
+ * kernels write (the scratch memory a context takes from its workspace) go
+ * to a fixed array in the library's own device memory, GDN_STATIC_MAX_B
+ * words on each GPU, held until the process ends.  The call allocates
+ * nothing and does not synchronise.  It arms no commit and reports no
+ * verdicts (use a context for those).  B above GDN_STATIC_MAX_B is
+ * GDN_ERR_SHAPE.  Calls that overlap on one GPU race on that array; calls
+ * ordered on a stream do not.  GDN_VALIDATE and GDN_FORCE_SIMPLE do not
+ * apply. */
+#define GDN_STATIC_MAX_B 65536
+gdn_status gdn_tree_verify_static(const gdn_tree_dims* dims, const void* q, const void* k, const void* v,
+                                  const float* g, const float* beta, const int32_t* parent, const float* S0,
+                                  float* o, hipStream_t stream);
+
 /* Static English name of a status code. */
 const char* gdn_status_string(gdn_status status);
 

@@ -172,3 +172,24 @@ def test_tree_build_arg_checks(lib):
         args[i] = FAKE + 4
         assert gdn.STATUS[lib.gdn_tree_build(ctypes.byref(d), *args)] == "GDN_ERR_ALIGN"
     assert lib.gdn_tree_build(ctypes.byref(dims(N=0)), *ok) == 0
+
+
+def test_verify_static_arg_checks(lib):
+    """the allocation-free verify rejects B beyond its fixed scratch, bad
+    shapes, NULL and misaligned pointers, all on the host"""
+    ptrs = [FAKE] * 8 + [None]
+    limit = int(re.search(r"#define GDN_STATIC_MAX_B (\d+)", open(HEADER).read()).group(1))
+    assert gdn.STATUS[lib.gdn_tree_verify_static(ctypes.byref(dims(B=limit + 1)), *ptrs)] == "GDN_ERR_SHAPE"
+    assert "at most %d" % limit in lib.gdn_last_error().decode()
+    assert gdn.STATUS[lib.gdn_tree_verify_static(None, *ptrs)] == "GDN_ERR_NULL"
+    for bad in (dict(N=257), dict(H_v=3), dict(d_k=96), dict(B=-1)):
+        assert gdn.STATUS[lib.gdn_tree_verify_static(ctypes.byref(dims(**bad)), *ptrs)] == "GDN_ERR_SHAPE"
+    assert gdn.STATUS[lib.gdn_tree_verify_static(ctypes.byref(dims(qkv_dtype=7)), *ptrs)] == "GDN_ERR_DTYPE"
+    for i in range(8):
+        args = list(ptrs)
+        args[i] = None
+        assert gdn.STATUS[lib.gdn_tree_verify_static(ctypes.byref(dims()), *args)] == "GDN_ERR_NULL"
+        args[i] = FAKE + 8
+        assert gdn.STATUS[lib.gdn_tree_verify_static(ctypes.byref(dims()), *args)] == "GDN_ERR_ALIGN"
+    assert lib.gdn_tree_verify_static(ctypes.byref(dims(B=0)), *ptrs) == 0
+    assert lib.gdn_tree_verify_static(ctypes.byref(dims(N=0)), *ptrs) == 0
