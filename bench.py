@@ -13,9 +13,10 @@ Inputs live in HBM before timing starts; R rotating input sets (>= 3x the
 
 Prints ONE JSON line.  `value` is nodes*heads per second of gdn_tree_verify
 (B*N*H_v per call over the timed calls).  Beside it: verify followed by
-gdn_commit_path (the accepted node's state) as one step, the roofline of the
-dominant kernel (verify, measured with HIP events on the stream it runs on)
-and the fp64 CPU oracle timed on this host.
+gdn_commit_path (the accepted node's state) as one step, the same step as
+the fused gdn_commit_verify (the previous tree's commit inside the next
+verify), the roofline of the dominant kernel (verify, measured with HIP
+events on the stream it runs on) and the fp64 CPU oracle timed on this host.
 """
 from __future__ import annotations
 
@@ -73,6 +74,17 @@ def commit_bytes(cfg, path_len) -> int:
     e = 2 if cfg.dtype == "bf16" else 4
     rows = int(sum(path_len))
     return (2 * B * Hv * dv * dk * 4 + rows * (Hk * dk * e + Hv * (dv * e + 8)) + B * N * 4 + B * 4)
+
+
+def commit_verify_bytes(cfg, path_len) -> int:
+    """Algorithmic bytes of one fused commit-then-verify: the verify's bytes,
+    plus the committed state written once (it is not read back), the
+    previous tree's accepted-path rows, parents and accepted nodes."""
+    B, N, Hk, Hv, dk, dv = cfg.B, cfg.N, cfg.H_k, cfg.H_v, cfg.d_k, cfg.d_v
+    e = 2 if cfg.dtype == "bf16" else 4
+    rows = int(sum(path_len))
+    return (verify_bytes(cfg) + B * Hv * dv * dk * 4 + rows * (Hk * dk * e + Hv * (dv * e + 8))
+            + B * N * 4 + B * 4)
 
 
 def read_traffic(kernel):
@@ -257,9 +269,29 @@ def main():
     def commit(s):
         gdn.gdn_commit_path(s["ctx"], s["accepted"], S_new=s["S_new"], stream=stream)
 
+    # fused commit-then-verify as a decoding chain: the tree recorded on
+    # fctx (set i) is committed at its accepted nodes inside the verify of
+    # set i + 1, the state alternating between two buffers
+    fctx = gdn.GdnContext.for_tensors(sets[0]["q"], sets[0]["v"], sets[0]["parent"])
+    fbufs = [torch.empty_like(sets[0]["S0"]) for _ in range(2)]
+    fstate = {"i": 0}
+
+    def fused_reset():
+        gdn.gdn_tree_verify(fctx, sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["g"], sets[0]["beta"],
+                            sets[0]["parent"], sets[0]["S0"], o=sets[0]["o"], stream=stream)
+        fstate["i"] = 0
+
+    def fused(_s=None):
+        i = fstate["i"]
+        prev, new = sets[i % len(sets)], sets[(i + 1) % len(sets)]
+        gdn.gdn_commit_verify(fctx, prev["accepted"], new["q"], new["k"], new["v"], new["g"], new["beta"],
+                              new["parent"], S_next=fbufs[i % 2], o=new["o"], stream=stream)
+        fstate["i"] = i + 1
+
     if args.kernel_only:
         # each kernel back to back, as the per-kernel event timing below runs it
-        for name, fn in (("verify", verify), ("commit", commit)):
+        fused_reset()
+        for name, fn in (("verify", verify), ("commit", commit), ("commit_verify", fused)):
             for i in range(args.warmup + args.steps):
                 fn(sets[i % len(sets)])
                 if i % 50 == 0:
@@ -330,6 +362,12 @@ def main():
 
     verify_dist = per_call(verify, args.steps)
     commit_dist = per_call(commit, args.steps)
+    fused_reset()
+    for _ in range(args.warmup):
+        fused()
+    fused_ms = timed(fused, args.steps)
+    fused_dist = per_call(fused, args.steps)
+    gdn.gdn_ctx_status(fctx)
 
     # context: a plain device copy (torch), read + write of 256 MiB each
     src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -350,6 +388,7 @@ def main():
     nh = cfg.B * cfg.N * cfg.H_v
     vbytes = verify_bytes(cfg)
     cbytes = float(np.mean([commit_bytes(cfg, pl) for pl in path_lens]))
+    fbytes = float(np.mean([commit_verify_bytes(cfg, pl) for pl in path_lens]))
     achieved = vbytes / (verify_ms * 1e-3) / 1e9
     vflops = verify_flops(cfg, float(np.mean([a["mean_strict_ancestors"] for a in anc_depth])))
     traffic = read_traffic("verify")
@@ -447,6 +486,12 @@ def main():
                    "algorithmic_bytes": vbytes, "GBps": achieved, "per_call": verify_dist},
         "step_verify_commit": {"ms": step_vc_ms, "nodes_heads_per_s": nh / (step_vc_ms * 1e-3),
                                "note": "gdn_tree_verify then gdn_commit_path, back to back"},
+        "step_commit_verify_fused": {
+            "ms": fused_ms, "per_call": fused_dist, "algorithmic_bytes": fbytes,
+            "GBps": fbytes / (fused_ms * 1e-3) / 1e9, "frac": fbytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "speedup_vs_separate": step_vc_ms / fused_ms,
+            "note": "gdn_commit_verify: the previous tree's commit at its accepted nodes formed on chip inside "
+                    "the next tree's verify, the committed state written once and not read back"},
         "commit": {"ms": commit_ms, "per_call": commit_dist, "algorithmic_bytes": cbytes,
                    "GBps": cbytes / (commit_ms * 1e-3) / 1e9,
                    "frac": cbytes / (commit_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "traffic": read_traffic("commit")},

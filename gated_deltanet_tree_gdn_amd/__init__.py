@@ -23,7 +23,7 @@ GDN_BF16, GDN_F32 = 0, 1
 STATUS = ["GDN_OK", "GDN_ERR_NULL", "GDN_ERR_SHAPE", "GDN_ERR_DTYPE", "GDN_ERR_ALIGN",
           "GDN_ERR_WORKSPACE", "GDN_ERR_TREE", "GDN_ERR_ACCEPT", "GDN_ERR_STATE", "GDN_ERR_HIP"]
 EXPORTS = ["gdn_tree_workspace_bytes", "gdn_ctx_create", "gdn_ctx_destroy", "gdn_tree_verify",
-           "gdn_tree_verify_branches", "gdn_commit_path", "gdn_tree_ancestors", "gdn_accept_path", "gdn_tree_build", "gdn_tree_verify_static", "gdn_ctx_status",
+           "gdn_tree_verify_branches", "gdn_commit_path", "gdn_commit_verify", "gdn_tree_ancestors", "gdn_accept_path", "gdn_tree_build", "gdn_tree_verify_static", "gdn_ctx_status",
            "gdn_status_string", "gdn_last_error"]
 
 
@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdn_accept_path.restype = i32
     lib.gdn_tree_build.argtypes = [dp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gdn_tree_build.restype = i32
+    lib.gdn_commit_verify.argtypes = [vp] * 11
+    lib.gdn_commit_verify.restype = i32
     lib.gdn_tree_verify_static.argtypes = [dp] + [vp] * 9
     lib.gdn_tree_verify_static.restype = i32
     lib.gdn_ctx_status.argtypes = [vp, vp]
@@ -220,6 +222,34 @@ def gdn_commit_path(ctx: GdnContext, accepted, S_new=None, stream=None):
     _require(S_new, "S_new", torch.float32, (d.B, d.H_v, d.d_v, d.d_k))
     _check(load_library().gdn_commit_path(ctx.handle, _ptr(accepted), _ptr(S_new), _stream(stream)))
     return S_new
+
+
+def gdn_commit_verify(ctx: GdnContext, accepted, q, k, v, g, beta, parent, S_next=None, o=None, stream=None):
+    """(o, S_next): the delayed commit of the tree recorded on ``ctx`` at
+    ``accepted`` fused into the verify of the new tree (q .. parent) on the
+    committed state.  ``S_next`` may be the recorded S0 tensor (in place).
+    Afterwards ``ctx`` records the new tree with S0 = S_next."""
+    torch = _torch()
+    d = ctx.dims
+    B, N, Hk, Hv, dk, dv = d.B, d.N, d.H_k, d.H_v, d.d_k, d.d_v
+    qkv = torch.bfloat16 if d.qkv_dtype == GDN_BF16 else torch.float32
+    _require(accepted, "accepted", torch.int32, (B,))
+    _require(q, "q", qkv, (B, N, Hk, dk))
+    _require(k, "k", qkv, (B, N, Hk, dk))
+    _require(v, "v", qkv, (B, N, Hv, dv))
+    _require(g, "g", torch.float32, (B, N, Hv))
+    _require(beta, "beta", torch.float32, (B, N, Hv))
+    _require(parent, "parent", torch.int32, (B, N))
+    if S_next is None:
+        S_next = torch.empty((B, Hv, dv, dk), dtype=torch.float32, device=q.device)
+    _require(S_next, "S_next", torch.float32, (B, Hv, dv, dk))
+    if o is None:
+        o = torch.empty((B, N, Hv, dv), dtype=torch.float32, device=q.device)
+    _require(o, "o", torch.float32, (B, N, Hv, dv))
+    _check(load_library().gdn_commit_verify(ctx.handle, _ptr(accepted), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                            _ptr(beta), _ptr(parent), _ptr(S_next), _ptr(o), _stream(stream)))
+    ctx._keep = (k, v, g, beta, parent, S_next)
+    return o, S_next
 
 
 def gdn_tree_ancestors(parent, stream=None):

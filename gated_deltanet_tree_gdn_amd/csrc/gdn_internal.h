@@ -47,13 +47,31 @@ struct CommitArgs {
     int force_walk;          // 1: per-node path walk even for bf16 (GDN_FORCE_SIMPLE=1)
 };
 
+// The previous tree of a fused commit-then-verify: its inputs (same B, N and
+// heads as the tree being verified), the state it started from, the
+// accepted node per sequence, and where the committed state goes (the
+// verify's S0).
+struct CommitPrev {
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const int32_t* parent;
+    const float* S0;
+    const int32_t* accepted;
+    float* S_next;
+    int32_t* accept_status;  // [B]: 0 or GDN_ERR_ACCEPT
+};
+
 // Verify dispatch: the MFMA path for bf16 q/k/v, the per-node walk otherwise.
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // The MFMA verify for bf16 and N <= 128.
 hipError_t launch_verify_ws(const VerifyArgs& a, hipStream_t stream);
 // Item-per-workgroup MFMA verify (bf16, N <= 128); not dispatched by
-// launch_verify, kept for the fused commit-then-verify path.
+// launch_verify.  With a CommitPrev it first commits the previous tree's
+// accepted path into c.S_next (== a.S0) and verifies on that state.
 hipError_t launch_verify_item(const VerifyArgs& a, hipStream_t stream);
+hipError_t launch_commit_verify(const VerifyArgs& a, const CommitPrev& c, hipStream_t stream);
 // Per-branch recurrent verification (the comparison baseline).
 hipError_t launch_verify_branches(const VerifyArgs& a, hipStream_t stream);
 // Sets the calling thread's detail message (gdn_last_error).

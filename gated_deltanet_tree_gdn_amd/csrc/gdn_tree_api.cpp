@@ -222,6 +222,63 @@ gdn_status gdn_commit_path(gdn_ctx* ctx, const int32_t* accepted, float* S_new, 
     return ok();
 }
 
+gdn_status gdn_commit_verify(gdn_ctx* ctx, const int32_t* accepted, const void* q, const void* k, const void* v,
+                             const float* g, const float* beta, const int32_t* parent, float* S_next, float* o,
+                             hipStream_t stream) {
+    if (!ctx) return fail(GDN_ERR_NULL, "ctx is NULL");
+    if (!ctx->have_verify) return fail(GDN_ERR_STATE, "gdn_commit_verify without a prior gdn_tree_verify");
+    const gdn_tree_dims d = ctx->dims;
+    auto record = [&]() {
+        ctx->have_verify = true;
+        ctx->have_commit = d.B > 0;
+        ctx->k = k; ctx->v = v; ctx->g = g; ctx->beta = beta; ctx->parent = parent; ctx->S0 = S_next;
+    };
+    if (d.B == 0) {
+        record();
+        return ok();
+    }
+    GDN_TRY(check_ptr(accepted, "accepted"));
+    GDN_TRY(check_ptr(S_next, "S_next"));
+    GDN_TRY(check_ptr(ctx->S0, "S0 of the recorded verify"));
+    if (d.N > 0) {
+        GDN_TRY(check_ptr(q, "q"));
+        GDN_TRY(check_ptr(k, "k"));
+        GDN_TRY(check_ptr(v, "v"));
+        GDN_TRY(check_ptr(g, "g"));
+        GDN_TRY(check_ptr(beta, "beta"));
+        GDN_TRY(check_ptr(parent, "parent"));
+        GDN_TRY(check_ptr(o, "o"));
+    }
+    if (ctx->validate) {
+        GDN_TRY(host_check_accepted(d, accepted, stream));
+        if (d.N > 0) GDN_TRY(host_check_tree(d, parent, stream));
+    }
+    gdn::CommitArgs ca{d.B, d.N, d.H_k, d.H_v, d.d_k, d.d_v, d.qkv_dtype, ctx->k, ctx->v, ctx->g, ctx->beta,
+                       ctx->parent, ctx->S0, accepted, S_next, ctx->status + d.B, ctx->force_walk ? 1 : 0};
+    hipError_t e = hipSuccess;
+    if (d.N == 0) {
+        e = gdn::launch_commit(ca, stream);
+    } else {
+        gdn::VerifyArgs va{d.B, d.N, d.H_k, d.H_v, d.d_k, d.d_v, d.qkv_dtype, q, k, v, g, beta, parent, S_next, o,
+                           ctx->status, ctx->force_walk ? 1 : 0};
+        if (d.qkv_dtype == GDN_BF16 && d.N <= 128 && !ctx->force_walk) {
+            gdn::CommitPrev cp{ctx->k, ctx->v, ctx->g, ctx->beta, ctx->parent, ctx->S0, accepted, S_next,
+                               ctx->status + d.B};
+            e = gdn::launch_commit_verify(va, cp, stream);
+        } else {
+            e = gdn::launch_commit(ca, stream);
+            if (e == hipSuccess) e = gdn::launch_verify(va, stream);
+        }
+    }
+    if (e != hipSuccess) {
+        ctx->have_verify = false;
+        ctx->have_commit = false;
+        return hip_fail(e, "commit-verify launch");
+    }
+    record();
+    return ok();
+}
+
 gdn_status gdn_tree_ancestors(const gdn_tree_dims* dims, const int32_t* parent, uint32_t* anc,
                               int32_t* depth, int32_t* tree_status, hipStream_t stream) {
     if (!dims) return fail(GDN_ERR_NULL, "dims is NULL");

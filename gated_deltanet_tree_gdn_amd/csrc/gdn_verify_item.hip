@@ -38,6 +38,24 @@
 //
 // Trees with a root path longer than 16 nodes, or more ancestor pairs than
 // the area holds, are verified by the per-node walk of gdn_walk.h.
+//
+// Fused commit (CMT): the delayed state commitment of the previous tree
+// (same page, section 3: the state is committed once the accepted branch is
+// known, at the next decoding step) runs inside the next tree's verify, so
+// the committed state is formed in registers, written once, and used by
+// the verify without being read back.  Along the previous tree's root path
+// to its accepted node, taken in chunks of at most 16 nodes (root first,
+// chunk-relative log-gate sums G, gamma = exp(G), D_ts = exp(G_t - G_s)):
+//     X_ts = beta_t D_ts (k_t . k_s)  (s < t),
+//     T' = diag(D_{n-1, .}) (I + X)^-1 diag(beta)   (n nodes in the chunk),
+//     S <- gamma_{n-1} S + K^T T' (V - gamma o (K S^T)),
+// which is the GDN delta rule applied node by node along the chunk.  One
+// otherwise idle wavefront walks the accepted path, stages the chunk's K
+// rows, and forms T' (16 lanes, one column each, by forward substitution)
+// while the tree is solved; every wavefront then applies the chunk to its
+// own 16 state rows on MFMA (K S^T with S as bf16 hi + lo, T' and the
+// right-hand side as hi + lo, K^T from K by transposing MFMAs against the
+// identity).
 
 #include <hip/hip_runtime.h>
 
@@ -64,7 +82,7 @@ __host__ __device__ constexpr int vi_zblocks(int I) {
 __host__ __device__ constexpr int vi_align(int x, int a) { return (x + a - 1) / a * a; }
 __host__ __device__ constexpr int vi_max(int x, int y) { return x > y ? x : y; }
 
-template <int NMAX, int DK, int DV>
+template <int NMAX, int DK, int DV, bool CMT>
 struct ItemLds {
     static constexpr int NTMAX = NMAX / 16;
     static constexpr int AW = NMAX / 32;
@@ -99,14 +117,24 @@ struct ItemLds {
     static constexpr int GAM = vi_align(vi_max(AREA + AREA_BYTES, FB_END), 16);  // float[NMAX]: gamma
     static constexpr int BET = GAM + 4 * NMAX;         // float[NMAX]: beta (kept past the tree phase)
     static constexpr int MISC = BET + 4 * NMAX;        // int[16]
-    static constexpr int TOTAL = MISC + 64;
+    // fused commit: one chunk of the previous tree's accepted path
+    static constexpr int CK = MISC + 64;               // bf16[16][DK]: K rows (k-slot order, swizzled)
+    static constexpr int CX = CK + 32 * DK;            // float[16][16]: X
+    static constexpr int CT = CX + 1024;               // bf16[16][16] T' hi, then lo
+    static constexpr int CG = CT + 1024;               // float[16]: G
+    static constexpr int CB = CG + 64;                 // float[16]: beta
+    static constexpr int CPAR = CB + 64;               // int8[NMAX]: parents of the previous tree
+    static constexpr int CPATH = CPAR + NMAX;          // uint8[NMAX]: accepted .. root
+    static constexpr int CMISC = CPATH + NMAX;         // int[4]: 0 path length, 1 accepted node
+    static constexpr int TOTAL = CMT ? CMISC + 16 : MISC + 64;
     static_assert(TOTAL <= 80 * 1024, "two workgroups per compute unit");
+    static_assert(!CMT || NMAX <= 128, "parents of the previous tree as int8");
     // misc[]: 1 a path longer than ZR (1), 2 an invalid parent (1)
 };
 
-template <int NMAX, int DK, int DV>
-__global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(VerifyArgs a) {
-    using L = ItemLds<NMAX, DK, DV>;
+template <int NMAX, int DK, int DV, bool CMT>
+__global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(VerifyArgs a, CommitPrev c) {
+    using L = ItemLds<NMAX, DK, DV, CMT>;
     constexpr int NW = DV / 16;          // wavefronts, 16 value columns each
     constexpr int NTH = 64 * NW;
     constexpr int KS = DK / 32;
@@ -117,6 +145,8 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     constexpr int ZR = L::ZR;            // root paths solved in registers
     static_assert(NMAX <= NTH, "one node per thread");
     static_assert(RT * NW >= NTMAX && RT <= 2, "Gram row tiles");
+    constexpr int PW = NW - 1;           // the commit's preparing wavefront
+    static_assert(64 * PW >= NMAX, "the preparing wavefront holds no tree node");
 
     __shared__ __align__(16) unsigned char smem[L::TOTAL];
     GDN_ITEM_PHASE_DECL
@@ -173,19 +203,27 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + L::TMASK);
     float* gam = reinterpret_cast<float*>(smem + L::GAM);
     int* misc = reinterpret_cast<int*>(smem + L::MISC);
+    unsigned char* CKb = smem + L::CK;
+    float* cx = reinterpret_cast<float*>(smem + L::CX);
+    uint16_t* ct = reinterpret_cast<uint16_t*>(smem + L::CT);
+    float* cg = reinterpret_cast<float*>(smem + L::CG);
+    float* cb = reinterpret_cast<float*>(smem + L::CB);
+    int8_t* cpar = reinterpret_cast<int8_t*>(smem + L::CPAR);
+    uint8_t* cpath = smem + L::CPATH;
+    int* cmisc = reinterpret_cast<int*>(smem + L::CMISC);
 
     // Natural 16-byte chunk c (elements 8c .. 8c + 7) of row `row` of K or Q
     // into the buffer, in the k-slot order the MFMA fragments read: element
     // 32 ks + 16 h + 4 g + r at position 32 ks + 8 g + 4 h + r, chunk 4 ks + g
     // stored at chunk position (4 ks + g) ^ (row mod CH); rows past N are zero
-    auto put_chunk = [&](int row, int c, uint4 v) {
-        const uint32_t keep = row < N ? 0xFFFFFFFFu : 0u;
+    auto put_chunk_at = [&](unsigned char* base, int row, int c, uint4 v, uint32_t keep) {
         const int sw = row & (CH - 1);
         const int ks = c >> 2, m = c & 3, hh = m >> 1, g0 = (m & 1) << 1;
         const int rbase = row * (DK * 2) + 8 * hh;
-        *reinterpret_cast<uint2*>(KQb + rbase + (((4 * ks + g0) ^ sw) << 4)) = make_uint2(v.x & keep, v.y & keep);
-        *reinterpret_cast<uint2*>(KQb + rbase + (((4 * ks + g0 + 1) ^ sw) << 4)) = make_uint2(v.z & keep, v.w & keep);
+        *reinterpret_cast<uint2*>(base + rbase + (((4 * ks + g0) ^ sw) << 4)) = make_uint2(v.x & keep, v.y & keep);
+        *reinterpret_cast<uint2*>(base + rbase + (((4 * ks + g0 + 1) ^ sw) << 4)) = make_uint2(v.z & keep, v.w & keep);
     };
+    auto put_chunk = [&](int row, int c, uint4 v) { put_chunk_at(KQb, row, c, v, row < N ? 0xFFFFFFFFu : 0u); };
     constexpr int KCH = NMAX * CH / NTH > 0 ? NMAX * CH / NTH : 1;   // chunks per thread
     static_assert(KCH * NTH >= NMAX * CH, "K/Q staging");
     auto stage = [&](const uint16_t* src) {
@@ -204,6 +242,202 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     };
     auto frag = [&](int row, int ks) -> bf16x8 {
         return load_frag(KQb + row * (DK * 2) + (((4 * ks + lg) ^ (row & (CH - 1))) << 4));
+    };
+    auto cfrag = [&](int row, int ks) -> bf16x8 {
+        return load_frag(CKb + row * (DK * 2) + (((4 * ks + lg) ^ (row & (CH - 1))) << 4));
+    };
+
+    // ------------------------------------------------ fused commit
+    // One chunk of the accepted path, from root-first position c0 on, by the
+    // calling wavefront: K rows into CK, G and beta, X, then T' (hi, lo).
+    auto commit_prep = [&](int c0) __attribute__((always_inline)) {
+        const int m = cmisc[0];
+        const int n = min(m - c0, 16);
+        const uint16_t* kp = static_cast<const uint16_t*>(c.k);
+        for (int e = lane; e < 16 * CH; e += 64) {
+            const int t = e / CH, ch = e % CH;
+            uint4 val = make_uint4(0u, 0u, 0u, 0u);
+            if (t < n) {
+                const int node = cpath[m - 1 - (c0 + t)];
+                val = *reinterpret_cast<const uint4*>(kp + ((static_cast<size_t>(b) * N + node) * Hk + kh) * DK + 8 * ch);
+            }
+            put_chunk_at(CKb, t, ch, val, 0xFFFFFFFFu);
+        }
+        float G = 0.f, bt = 0.f;
+        if (lane < n) {
+            const size_t nh = (static_cast<size_t>(b) * N + cpath[m - 1 - (c0 + lane)]) * Hv + h;
+            G = c.g[nh];
+            bt = c.beta[nh];
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const float x = __shfl_up(G, o, 16);
+            if ((lane & 15) >= o) G += x;
+        }
+        if (lane < 16) {
+            cg[lane] = G;
+            cb[lane] = bt;
+        }
+        WaveSync::sync();
+        // X_ts = beta_t D_ts (k_t . k_s), s < t < n; lane: t = 4 lg + r, s = lc
+        f32x4 gr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 af = cfrag(lc, ks);
+            gr = mfma(af, af, gr);
+        }
+        {
+            const float Gs = cg[lc];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 4 * lg + r;
+                cx[16 * t + lc] = lc < t && t < n ? cb[t] * __expf(cg[t] - Gs) * gr[r] : 0.f;
+            }
+        }
+        WaveSync::sync();
+        // column j of (I + X)^-1 by forward substitution, then
+        // T'_sj = D_{n-1, s} [(I + X)^-1]_sj beta_j
+        if (lane < 16) {
+            const int j = lane;
+            float y[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                // one row of X at a time (the opaque offset keeps the loads
+                // from being hoisted, which would hold every row at once)
+                int xo = 16 * t;
+                asm volatile("" : "+v"(xo));
+                float xr[16];
+#pragma unroll
+                for (int q = 0; q < (t + 3) / 4; ++q) {
+                    const f32x4 x4 = *reinterpret_cast<const f32x4*>(cx + xo + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) xr[4 * q + e] = x4[e];
+                }
+                float acc = t == j ? 1.f : 0.f;
+#pragma unroll
+                for (int s = 0; s < t; ++s) acc -= xr[s] * y[s];
+                // orders this row's result before the next row's offset
+                asm volatile("" : "+v"(acc));
+                y[t] = acc;
+            }
+            const float Gn = cg[max(n - 1, 0)];
+            const float bj = j < n ? cb[j] : 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const float tv = s < n ? __expf(Gn - cg[s]) * y[s] * bj : 0.f;
+                const __bf16 th = static_cast<__bf16>(tv);
+                const __bf16 tl = static_cast<__bf16>(tv - static_cast<float>(th));
+                ct[16 * s + j] = __builtin_bit_cast(uint16_t, th);
+                ct[256 + 16 * s + j] = __builtin_bit_cast(uint16_t, tl);
+            }
+        }
+    };
+    // The prepared chunk from root-first position c0 applied to this
+    // wavefront's 16 state rows s0 (the layout of s0r below); cvr: this
+    // lane's piece of the chunk's V row lc (value columns col0 + 4 lg .. + 3)
+    auto commit_apply = [&](float4 (&s0)[2 * KS], int c0, uint2 cvr, const s16x4& eye) __attribute__((always_inline)) {
+        const int m = cmisc[0];
+        const int n = min(m - c0, 16);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        // P_tc = k_t . S_c (lane: t = 4 lg + r, value row c = lc), S as hi + lo
+        f32x4 ph = zero, pl = zero;
+        bf16x8 af[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            af[ks] = cfrag(lc, ks);
+            const float4 x0 = s0[2 * ks], x1 = s0[2 * ks + 1];
+            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            bf16x8 hi, lo;
+            split8(x, hi, lo);
+            ph = mfma(af[ks], hi, ph);
+            pl = mfma(af[ks], lo, pl);
+        }
+        // right-hand side V - gamma o P (zero past the chunk), as hi + lo
+        const f32x4 vt = mfma16(__builtin_bit_cast(s16x4, cvr), eye, zero);
+        s16x4 rh4, rl4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * lg + r;
+            const float rv = t < n ? vt[r] - __expf(cg[t]) * (ph[r] + pl[r]) : 0.f;
+            const __bf16 hv = static_cast<__bf16>(rv);
+            rh4[r] = __builtin_bit_cast(short, hv);
+            rl4[r] = __builtin_bit_cast(short, static_cast<__bf16>(rv - static_cast<float>(hv)));
+        }
+        // W = T' (V - gamma o P): lane s = 4 lg + r, c = lc, the B operand
+        // layout of the update
+        const s16x4 th4 = *reinterpret_cast<const s16x4*>(ct + 16 * lc + 4 * lg);
+        const s16x4 tl4 = *reinterpret_cast<const s16x4*>(ct + 256 + 16 * lc + 4 * lg);
+        f32x4 w = mfma16(th4, rh4, zero);
+        w = mfma16(tl4, rh4, w);
+        w = mfma16(th4, rl4, w);
+        s16x4 wh4, wl4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const __bf16 hv = static_cast<__bf16>(w[r]);
+            wh4[r] = __builtin_bit_cast(short, hv);
+            wl4[r] = __builtin_bit_cast(short, static_cast<__bf16>(w[r] - static_cast<float>(hv)));
+        }
+        // S <- gamma_{n-1} S + K^T W per 16-column block q of d_k: the A
+        // operand k_{4 lg + r}[16 q + lc] is the fragment of K row lc
+        // transposed by an MFMA against the identity (exact: bf16 values)
+        const float gl = __expf(cg[max(n - 1, 0)]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint4 au = __builtin_bit_cast(uint4, af[ks]);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const s16x4 ain = __builtin_bit_cast(s16x4, hf == 0 ? make_uint2(au.x, au.y) : make_uint2(au.z, au.w));
+                const f32x4 kt = mfma16(ain, eye, zero);
+                s16x4 ka;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ka[r] = __builtin_bit_cast(short, static_cast<__bf16>(kt[r]));
+                f32x4 acc = __builtin_bit_cast(f32x4, s0[2 * ks + hf]) * gl;
+                acc = mfma16(ka, wh4, acc);
+                acc = mfma16(ka, wl4, acc);
+                s0[2 * ks + hf] = __builtin_bit_cast(float4, acc);
+            }
+        }
+    };
+    // V piece of the chunk at c0 for commit_apply (row lc of the chunk)
+    auto commit_v = [&](int c0, int col) __attribute__((always_inline)) -> uint2 {
+        const int m = cmisc[0];
+        const int t = min(c0 + lc, m - 1);
+        const size_t nh = (static_cast<size_t>(b) * N + cpath[m - 1 - t]) * Hv + h;
+        return *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(c.v) + nh * DV + col + 4 * lg);
+    };
+    // Every chunk of the path.  `ready0`: chunk 0 is prepared and s0 holds
+    // the previous state; otherwise both happen here.  Between chunks the
+    // state goes out to S_next and comes back (each lane reads what it
+    // wrote), so that no state registers are held across a preparation.
+    auto commit_all = [&](float4 (&s0)[2 * KS], int col, bool ready0, uint2 cvr0, const s16x4& eye)
+                          __attribute__((always_inline)) {
+        const int m = cmisc[0];
+        const float* prev = c.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + col + lc) * DK + 4 * lg;
+        float* next = c.S_next + ((static_cast<size_t>(b) * Hv + h) * DV + col + lc) * DK + 4 * lg;
+        for (int c0 = 0; c0 < m; c0 += 16) {
+            // lane indices through an opaque copy: LDS addresses are then
+            // formed per chunk instead of held across the loop
+            refresh();
+            if (c0 > 0 || !ready0) {
+                __syncthreads();   // the previous chunk is applied
+                if (wave == 0) commit_prep(c0);
+                __syncthreads();
+                __threadfence();   // this lane's stores of the state are visible to its loads
+                const float4* src = reinterpret_cast<const float4*>(c0 == 0 ? prev : next);
+#pragma unroll
+                for (int q = 0; q < 2 * KS; ++q) s0[q] = src[4 * q];
+            }
+            commit_apply(s0, c0, (ready0 && c0 == 0) ? cvr0 : commit_v(c0, col), eye);
+            if (c0 + 16 < m) {
+#pragma unroll
+                for (int q = 0; q < 2 * KS; ++q) reinterpret_cast<float4*>(next)[4 * q] = s0[q];
+            }
+        }
+    };
+    auto commit_store = [&](const float4 (&s0)[2 * KS], int col) __attribute__((always_inline)) {
+        float4* dst = reinterpret_cast<float4*>(c.S_next + ((static_cast<size_t>(b) * Hv + h) * DV + col + lc) * DK + 4 * lg);
+#pragma unroll
+        for (int q = 0; q < 2 * KS; ++q) dst[4 * q] = s0[q];
     };
 
     // ------------------------------------------------ (1) scalars, K, Q rows
@@ -226,6 +460,24 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
         gv[i] = gi;
         bet[i] = bi;
         if (tid < NTMAX) tmask[tid] = 0u;
+        if constexpr (CMT) {
+            // the previous tree's parents (outside [-1, i - 1]: read as -1)
+            int pp = -1;
+            if (i < N) {
+                pp = c.parent[static_cast<size_t>(b) * N + i];
+                if (pp < -1 || pp >= i) pp = -1;
+            }
+            cpar[i] = static_cast<int8_t>(pp);
+        }
+    }
+    if constexpr (CMT) {
+        if (tid == NTH - 1) {
+            // an accepted node out of range is reported and read as -1
+            int acc = c.accepted[b];
+            const bool badacc = acc < -1 || acc >= N;
+            if (h == 0) c.accept_status[b] = badacc ? GDN_ERR_ACCEPT : 0;
+            cmisc[1] = badacc ? -1 : acc;
+        }
     }
     // Q rows of this wavefront's Gram row tiles, in the k-slot order of the
     // buffer, loaded now so that they arrive with K
@@ -274,6 +526,13 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
 #pragma unroll
         for (int w = 0; w < L::AW; ++w) anc[i * L::AW + w] = bits[w];
     }
+    if constexpr (CMT) {
+        if (tid == 64 * PW) {
+            int mm = 0;
+            for (int s = cmisc[1]; s >= 0; s = cpar[s]) cpath[mm++] = static_cast<uint8_t>(s);
+            cmisc[0] = mm;
+        }
+    }
     __syncthreads();
     const bool fast = misc[1] == 0;
     if (h == 0 && tid == 0) a.tree_status[b] = misc[2] ? GDN_ERR_TREE : 0;
@@ -281,6 +540,24 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     if (!fast) {
         // a path longer than ZR: the per-node walk, one wavefront per
         // 64-column slice in turn (the others have nothing to do for this item)
+        if constexpr (CMT) {
+            // the committed state first: the walk reads it back from a.S0
+            refresh();
+            const int col = NW == 8 ? 32 * (wave & 3) + 16 * (wave >> 2) : 16 * wave;
+            float4 s0c[2 * KS];
+            if (cmisc[0] == 0) {
+                const float4* src = reinterpret_cast<const float4*>(
+                    c.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + col + lc) * DK + 4 * lg);
+#pragma unroll
+                for (int q = 0; q < 2 * KS; ++q) s0c[q] = src[4 * q];
+            }
+            s16x4 eye;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) eye[q] = 4 * lg + q == lc ? static_cast<short>(0x3F80) : short(0);
+            commit_all(s0c, col, false, make_uint2(0u, 0u), eye);
+            commit_store(s0c, col);
+            __threadfence();
+        }
         __syncthreads();   // every read of the tree arrays is done
         if (wave == 0) {
             int* par_s = reinterpret_cast<int*>(smem + L::FB_PAR);
@@ -385,6 +662,9 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     // where X_{p_d, p_e} sits at slot e - d of row p_d; y_d = D_{i, p_d}
     // (q_i . k_{p_d}); the scaling z_d *= beta_{p_d} follows in (6)
     GDN_ITEM_PHASE(4);
+    if constexpr (CMT) {
+        if (wave == PW && cmisc[0] > 0) commit_prep(0);
+    }
     float z[ZR];
     if (tid < N) {
         const int i = tid;
@@ -416,15 +696,26 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     const int col0 = NW == 8 ? 32 * (wave & 3) + 16 * (wave >> 2) : 16 * wave;
     float4 s0r[2 * KS];
     uint2 vr[NTMAX];
-    {
-        const float4* src = reinterpret_cast<const float4*>(
-            a.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + col0 + lc) * DK + 4 * lg);
-#pragma unroll
-        for (int q = 0; q < 2 * KS; ++q) s0r[q] = src[4 * q];
+    uint2 cvr0 = make_uint2(0u, 0u);
+    auto load_v = [&]() __attribute__((always_inline)) {
         const uint16_t* vsrc = vg + static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV + col0 + 4 * lg;
 #pragma unroll
         for (int S = 0; S < NTMAX; ++S)
             vr[S] = *reinterpret_cast<const uint2*>(vsrc + static_cast<size_t>(min(16 * S + lc, N - 1)) * Hv * DV);
+    };
+    // fused commit: an accepted path of more than one chunk is applied
+    // after the Z~ scatter with the V loads held back (its chunk
+    // preparations run in between and need the registers)
+    const int cm = CMT ? cmisc[0] : 0;
+    {
+        const float4* src = reinterpret_cast<const float4*>(
+            (CMT ? c.S0 : a.S0) + ((static_cast<size_t>(b) * Hv + h) * DV + col0 + lc) * DK + 4 * lg);
+#pragma unroll
+        for (int q = 0; q < 2 * KS; ++q) s0r[q] = src[4 * q];
+        if (cm <= 16) load_v();
+        if constexpr (CMT) {
+            if (cm > 0) cvr0 = commit_v(0, col0);
+        }
     }
     __syncthreads();   // every read of the tree arrays is done
     for (int e = tid; e < L::ZD_BYTES / 16; e += NTH) reinterpret_cast<uint4*>(Zd)[e] = make_uint4(0u, 0u, 0u, 0u);
@@ -451,6 +742,19 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
 
     // ------------------------------------------------ (7) R'
     GDN_ITEM_PHASE(6);
+    // identity for the transposes: lane (n, g) holds B[4 g + j][n]
+    s16x4 eye;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) eye[q] = 4 * lg + q == lc ? static_cast<short>(0x3F80) : short(0);
+    if constexpr (CMT) {
+        if (cm > 16) {
+            commit_all(s0r, col0, true, cvr0, eye);
+            load_v();
+        } else if (cm > 0) {
+            commit_apply(s0r, 0, cvr0, eye);
+        }
+        commit_store(s0r, col0);
+    }
     bf16x8 s0h[KS], s0l[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -458,10 +762,6 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
         const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         split8(x, s0h[ks], s0l[ks]);
     }
-    // identity for the V transpose: lane (n, g) holds B[4 g + j][n]
-    s16x4 eye;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) eye[q] = 4 * lg + q == lc ? static_cast<short>(0x3F80) : short(0);
     bf16x8 rh[NKMAX], rl[NKMAX];
 #pragma unroll
     for (int kap = 0; kap < NKMAX; ++kap) {
@@ -534,22 +834,31 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     GDN_ITEM_PHASE_END;
 }
 
-}  // namespace
-
-hipError_t launch_verify_item(const VerifyArgs& a, hipStream_t stream) {
+template <bool CMT>
+hipError_t launch_item(const VerifyArgs& a, const CommitPrev& c, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.B) * a.H_v);
     auto go = [&](auto kern, int dv) {
-        hipLaunchKernelGGL(kern, grid, dim3(4 * dv), 0, stream, a);
+        hipLaunchKernelGGL(kern, grid, dim3(4 * dv), 0, stream, a, c);
         return hipGetLastError();
     };
     if (a.N <= 64) {
         if (a.d_k == 64)
-            return a.d_v == 64 ? go(verify_item_kernel<64, 64, 64>, 64) : go(verify_item_kernel<64, 64, 128>, 128);
-        return a.d_v == 64 ? go(verify_item_kernel<64, 128, 64>, 64) : go(verify_item_kernel<64, 128, 128>, 128);
+            return a.d_v == 64 ? go(verify_item_kernel<64, 64, 64, CMT>, 64) : go(verify_item_kernel<64, 64, 128, CMT>, 128);
+        return a.d_v == 64 ? go(verify_item_kernel<64, 128, 64, CMT>, 64) : go(verify_item_kernel<64, 128, 128, CMT>, 128);
     }
     if (a.d_k == 64)
-        return a.d_v == 64 ? go(verify_item_kernel<128, 64, 64>, 64) : go(verify_item_kernel<128, 64, 128>, 128);
-    return a.d_v == 64 ? go(verify_item_kernel<128, 128, 64>, 64) : go(verify_item_kernel<128, 128, 128>, 128);
+        return a.d_v == 64 ? go(verify_item_kernel<128, 64, 64, CMT>, 64) : go(verify_item_kernel<128, 64, 128, CMT>, 128);
+    return a.d_v == 64 ? go(verify_item_kernel<128, 128, 64, CMT>, 64) : go(verify_item_kernel<128, 128, 128, CMT>, 128);
+}
+
+}  // namespace
+
+hipError_t launch_verify_item(const VerifyArgs& a, hipStream_t stream) {
+    return launch_item<false>(a, CommitPrev{}, stream);
+}
+
+hipError_t launch_commit_verify(const VerifyArgs& a, const CommitPrev& c, hipStream_t stream) {
+    return launch_item<true>(a, c, stream);
 }
 
 }  // namespace gdn

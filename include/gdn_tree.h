@@ -69,7 +69,7 @@ typedef enum {
     GDN_ERR_WORKSPACE = 5, /* workspace missing or smaller than required           */
     GDN_ERR_TREE = 6,      /* some parent[b][i] outside [-1, i-1]                  */
     GDN_ERR_ACCEPT = 7,    /* some accepted[b] outside [-1, N-1]                   */
-    GDN_ERR_STATE = 8,     /* gdn_commit_path without a prior gdn_tree_verify      */
+    GDN_ERR_STATE = 8,     /* a commit without a prior gdn_tree_verify             */
     GDN_ERR_HIP = 9        /* a HIP runtime call or kernel launch failed           */
 } gdn_status;
 
@@ -142,6 +142,27 @@ gdn_status gdn_tree_verify_branches(gdn_ctx* ctx, const void* q, const void* k, 
  * Returns GDN_ERR_STATE if no verify was recorded on ctx. */
 gdn_status gdn_commit_path(gdn_ctx* ctx, const int32_t* accepted, float* S_new,
                            hipStream_t stream);
+
+/* The delayed commit fused into the next verify (same section: the state is
+ * committed at the next decoding step, once the accepted branch is known).
+ * Equivalent to gdn_commit_path(ctx, accepted, S_next) followed by
+ * gdn_tree_verify(ctx, q, k, v, g, beta, parent, S_next, o): S_next[b] is
+ * the state at accepted[b] of the tree recorded on ctx, and o is the new
+ * tree's output on that state.  For bf16 q/k/v and N <= 128 one kernel
+ * forms S_next on chip, writes it once and verifies on it without reading
+ * it back; other cases run the two steps in turn.
+ *   accepted        [B] int32, in [-1, N-1], for the recorded tree
+ *   q .. parent, o  the new tree, as in gdn_tree_verify (same dims)
+ *   S_next          [B][H_v][d_v][d_k] fp32, written; may be exactly the
+ *                   recorded S0 (in place), must not partially overlap any
+ *                   input
+ * Afterwards ctx records the new tree with S0 = S_next (for the next
+ * commit), and gdn_ctx_status reports both the accepted-node verdicts and
+ * the new tree's.  Returns GDN_ERR_STATE if no verify was recorded on ctx;
+ * a failed argument check leaves the record unchanged. */
+gdn_status gdn_commit_verify(gdn_ctx* ctx, const int32_t* accepted, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta, const int32_t* parent,
+                             float* S_next, float* o, hipStream_t stream);
 
 /* Ancestor sets of every node (the "ancestor relationships" the interaction
  * matrices follow, same section): anc[b][i] is a bit row of ceil(N/32)

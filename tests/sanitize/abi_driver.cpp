@@ -182,6 +182,51 @@ int main() {
     CHECK(gdn_commit_path(c, t.accepted, t.S_new, nullptr) == GDN_OK);
     CHECK(gdn_ctx_destroy(c) == GDN_OK);
 
+    // fused commit-then-verify: needs a recorded verify; for bf16 and N <= 128
+    // one launch with the recorded tree as the previous one; afterwards the
+    // new tree is recorded with S0 = S_next
+    {
+        CHECK(gdn_ctx_create(&d, work, ws, &c) == GDN_OK);
+        auto cv = [&](const int32_t* acc, float* s_next, float* o) {
+            return gdn_commit_verify(c, acc, t.q, t.k, t.v, t.g, t.beta, t.parent, s_next, o, nullptr);
+        };
+        CHECK(gdn_commit_verify(nullptr, t.accepted, t.q, t.k, t.v, t.g, t.beta, t.parent, t.S_new, t.o,
+                                nullptr) == GDN_ERR_NULL);
+        CHECK(cv(t.accepted, t.S_new, t.o) == GDN_ERR_STATE);
+        CHECK(verify(c, t) == GDN_OK);
+        const int nv = g_stub.verifies, nc = g_stub.commits;
+        CHECK(cv(nullptr, t.S_new, t.o) == GDN_ERR_NULL);
+        CHECK(cv(t.accepted, nullptr, t.o) == GDN_ERR_NULL);
+        CHECK(cv(t.accepted, t.S_new, nullptr) == GDN_ERR_NULL);
+        CHECK(cv(t.accepted, t.S_new + 1, t.o) == GDN_ERR_ALIGN);
+        CHECK(g_stub.commit_verifies == 0);
+        CHECK(cv(t.accepted, t.S_new, t.o) == GDN_OK && g_stub.commit_verifies == 1);
+        CHECK(g_stub.verifies == nv && g_stub.commits == nc);
+        CHECK(g_stub.last_prev.S0 == t.S0 && g_stub.last_prev.S_next == t.S_new && g_stub.last_verify.S0 == t.S_new);
+        CHECK(g_stub.last_prev.accepted == t.accepted && g_stub.last_prev.k == t.k && g_stub.last_verify.q == t.q);
+        CHECK(g_stub.last_prev.accept_status == g_stub.last_verify.tree_status + d.B);
+        // the record now holds S_next: the next commit starts from it
+        CHECK(gdn_commit_path(c, t.accepted, t.S0, nullptr) == GDN_OK && g_stub.last_commit.S0 == t.S_new);
+        g_stub.commit_verdict = GDN_ERR_ACCEPT;
+        CHECK(cv(t.accepted, t.S_new, t.o) == GDN_OK);
+        CHECK(gdn_ctx_status(c, nullptr) == GDN_ERR_ACCEPT);
+        g_stub.commit_verdict = 0;
+        g_stub.launch_error = hipErrorInvalidValue;
+        CHECK(cv(t.accepted, t.S_new, t.o) == GDN_ERR_HIP);
+        CHECK(gdn_commit_path(c, t.accepted, t.S_new, nullptr) == GDN_ERR_STATE);
+        g_stub.launch_error = hipSuccess;
+        CHECK(gdn_ctx_destroy(c) == GDN_OK);
+        // fp32 q/k/v: a commit launch, then a verify launch on S_next
+        const gdn_tree_dims f{3, 40, 2, 4, 128, 64, GDN_F32};
+        CHECK(gdn_ctx_create(&f, work, ws, &c) == GDN_OK);
+        CHECK(verify(c, t) == GDN_OK);
+        const int nv2 = g_stub.verifies, nc2 = g_stub.commits, ncv = g_stub.commit_verifies;
+        CHECK(cv(t.accepted, t.S_new, t.o) == GDN_OK);
+        CHECK(g_stub.verifies == nv2 + 1 && g_stub.commits == nc2 + 1 && g_stub.commit_verifies == ncv);
+        CHECK(g_stub.last_commit.S_new == t.S_new && g_stub.last_verify.S0 == t.S_new);
+        CHECK(gdn_ctx_destroy(c) == GDN_OK);
+    }
+
     // accepted-node selection and tree construction
     int32_t* target = static_cast<int32_t*>(dev_alloc(static_cast<size_t>(d.B) * (d.N + 1) * 4));
     int32_t* lens = static_cast<int32_t*>(dev_alloc(d.B * 4));

@@ -45,6 +45,17 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t) {
     return g_stub.launch_error;
 }
 
+hipError_t launch_commit_verify(const VerifyArgs& a, const CommitPrev& c, hipStream_t) {
+    ++g_stub.commit_verifies;
+    g_stub.last_verify = a;
+    g_stub.last_prev = c;
+    for (int b = 0; b < a.B; ++b) {
+        a.tree_status[b] = g_stub.verify_verdict;
+        c.accept_status[b] = g_stub.commit_verdict;
+    }
+    return g_stub.launch_error;
+}
+
 hipError_t launch_verify_branches(const VerifyArgs& a, hipStream_t) {
     ++g_stub.branch_verifies;
     g_stub.last_verify = a;
