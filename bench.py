@@ -35,9 +35,13 @@ METRIC = "GDN tree-verify nodes·heads/s per layer at B=32,N=128; % HBM/MFMA roo
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 WORKLOAD = "bestfirst_b32n128"
-KERNEL_SOURCES = ["gdn_tree_api.cpp", "gdn_internal.h", "gdn_mfma.h", "gdn_walk.h", "gdn_simple.hip",
-                  "gdn_fast.hip", "gdn_verify_ws.hip", "gdn_commit.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_verify_bestfirst_b32n128.json")
+KERNEL_SOURCES = ["gdn_internal.h", "gdn_mfma.h", "gdn_walk.h", "gdn_fast.hip", "gdn_verify_ws.hip",
+                  "gdn_verify_item.hip", "gdn_commit.hip"]
+STRESS = "stress48"
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"traffic_verify_{workload}.json")
 
 
 def kernel_source_sha() -> str:
@@ -87,12 +91,12 @@ def commit_verify_bytes(cfg, path_len) -> int:
             + B * N * 4 + B * 4)
 
 
-def read_traffic(kernel):
-    """HBM bytes of one launch of `kernel` ("verify" or "commit") from the
-    committed rocprofv3 counters, if they were taken on the current kernel
-    sources; else None."""
+def read_traffic(kernel, workload=WORKLOAD):
+    """HBM bytes of one launch of `kernel` ("verify", "commit" or
+    "commit_verify") on `workload` from the committed rocprofv3 counters, if
+    they were taken on the current kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -102,13 +106,17 @@ def read_traffic(kernel):
 
 
 COPY_CALLS = 5
-KERNELS = {"verify": "verify_ws_kernel", "commit": "commit_mfma_kernel", "copy": "MulFunctor"}
+# kernel-name patterns per role; the fused kernel is the item kernel's
+# commit instantiation (template flag true)
+KERNELS = {"verify": ("verify_ws_kernel", "verify_fast_kernel"), "commit": ("commit_mfma_kernel",),
+           "commit_verify": ("verify_item_kernel",), "copy": ("MulFunctor",)}
 
 
-def write_traffic(fetch_csv, write_csv, copy_mib):
+def write_traffic(fetch_csv, write_csv, copy_mib, workload):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each kernel, scaled by
     the factor that maps the same counter to the known bytes of the
-    calibration copy, written to TRAFFIC_FILE with the kernel sources' hash."""
+    calibration copy, written to the workload's traffic file with the kernel
+    sources' hash."""
     import csv
 
     def per_kernel(path, counter):
@@ -118,8 +126,8 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
         for r in rows:
             if r["Counter_Name"] != counter:
                 continue
-            for k, pat in KERNELS.items():
-                if pat in r["Kernel_Name"]:
+            for k, pats in KERNELS.items():
+                if any(pat in r["Kernel_Name"] for pat in pats):
                     vals[k].append(float(r["Counter_Value"]))
         vals["copy"] = vals["copy"][-COPY_CALLS:]
         return {k: (sum(v) / len(v) if v else None) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
@@ -130,13 +138,14 @@ def write_traffic(fetch_csv, write_csv, copy_mib):
     ff, fw = copy_kib / fetch["copy"], copy_kib / write["copy"]
     out = {"kernel_source_sha": kernel_source_sha(), "copy_kib": copy_kib,
            "fetch_factor": ff, "write_factor": fw, "dispatches": {"fetch": nf, "write": nw}}
-    for k in ("verify", "commit"):
+    out["workload"] = workload
+    for k in ("verify", "commit", "commit_verify"):
         if fetch[k] is None or write[k] is None:
             continue
         out[k] = {"fetch_kib": fetch[k], "write_kib": write[k],
                   "hbm_bytes_per_launch": 1024.0 * (fetch[k] * ff + write[k] * fw)}
     out["hbm_bytes_per_launch"] = out.get("verify", {}).get("hbm_bytes_per_launch")
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file(workload), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
 
@@ -207,13 +216,15 @@ def main():
                     help="profiler runs: verify + commit back to back, then the calibration copies; "
                          "prints progress, no JSON")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of each calibration copy (--kernel-only)")
+    ap.add_argument("--kernel-workload", default=WORKLOAD, choices=[WORKLOAD, STRESS],
+                    help="workload of --kernel-only and --traffic-from (default: the metric's)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter CSVs of a --kernel-only run into the "
                          "per-launch HBM traffic file read by this script")
     args = ap.parse_args()
 
     if args.traffic_from:
-        write_traffic(*args.traffic_from, copy_mib=args.copy_mib)
+        write_traffic(*args.traffic_from, copy_mib=args.copy_mib, workload=args.kernel_workload)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -232,14 +243,18 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = G.CONFIGS[WORKLOAD]
+    stress_only = args.kernel_only and args.kernel_workload == STRESS
+    cfg = G.CONFIGS[STRESS if stress_only else WORKLOAD]
     gdn.load_library()
 
+    # rotating input sets (three layers for the stress workload, seeded as in
+    # its context figure below)
     sets = []
-    for r in range(args.sets):
-        parent = G.make_tree(cfg, G.rng_for(args.seed, 1000 + r))
+    for r in range(3 if stress_only else args.sets):
+        tseed, aseed = (3000 + r, 4000 + r) if stress_only else (1000 + r, 2000 + r)
+        parent = G.make_tree(cfg, G.rng_for(args.seed, tseed))
         d = G.make_inputs_device(cfg, seed=args.seed, layer=r, parent=parent, device=dev)
-        d["accepted"] = torch.from_numpy(G.rng_for(args.seed, 2000 + r).integers(0, cfg.N, size=cfg.B)
+        d["accepted"] = torch.from_numpy(G.rng_for(args.seed, aseed).integers(0, cfg.N, size=cfg.B)
                                          .astype(np.int32)).to(dev)
         d["o"] = torch.empty((cfg.B, cfg.N, cfg.H_v, cfg.d_v), dtype=torch.float32, device=dev)
         d["S_new"] = torch.empty_like(d["S0"])
@@ -290,8 +305,11 @@ def main():
 
     if args.kernel_only:
         # each kernel back to back, as the per-kernel event timing below runs it
-        fused_reset()
-        for name, fn in (("verify", verify), ("commit", commit), ("commit_verify", fused)):
+        # (the fused kernel serves trees of up to 128 nodes)
+        if not stress_only:
+            fused_reset()
+        roles = (("verify", verify), ("commit", commit)) + (() if stress_only else (("commit_verify", fused),))
+        for name, fn in roles:
             for i in range(args.warmup + args.steps):
                 fn(sets[i % len(sets)])
                 if i % 50 == 0:
@@ -457,6 +475,7 @@ def main():
         stress = {"workload": "stress48 layer (B=64, N=256, H_v=32, H_k=16, d=128, depth<=24)",
                   "verify_us": sv_ms * 1e3, "commit_us": sc_ms * 1e3, "verify_algorithmic_bytes": sb,
                   "verify_GBps": sb / (sv_ms * 1e-3) / 1e9, "verify_frac_of_peak": sb / (sv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "verify_traffic": read_traffic("verify", STRESS),
                   "verify_nodes_heads_per_s": scfg.B * scfg.N * scfg.H_v / (sv_ms * 1e-3)}
         del ssets, sets
         torch.cuda.empty_cache()
@@ -489,7 +508,7 @@ def main():
         "step_commit_verify_fused": {
             "ms": fused_ms, "per_call": fused_dist, "algorithmic_bytes": fbytes,
             "GBps": fbytes / (fused_ms * 1e-3) / 1e9, "frac": fbytes / (fused_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "speedup_vs_separate": step_vc_ms / fused_ms,
+            "speedup_vs_separate": step_vc_ms / fused_ms, "traffic": read_traffic("commit_verify"),
             "note": "gdn_commit_verify: the previous tree's commit at its accepted nodes formed on chip inside "
                     "the next tree's verify, the committed state written once and not read back"},
         "commit": {"ms": commit_ms, "per_call": commit_dist, "algorithmic_bytes": cbytes,
