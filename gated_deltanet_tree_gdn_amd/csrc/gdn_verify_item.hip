@@ -145,8 +145,10 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     constexpr int ZR = L::ZR;            // root paths solved in registers
     static_assert(NMAX <= NTH, "one node per thread");
     static_assert(RT * NW >= NTMAX && RT <= 2, "Gram row tiles");
-    constexpr int PW = NW - 1;           // the commit's preparing wavefront
-    static_assert(64 * PW >= NMAX, "the preparing wavefront holds no tree node");
+    // the commit's preparing wavefront: the first one past the node threads
+    // (idle in the structure and X/Y phases, a light share of the Gram)
+    constexpr int PW = NMAX / 64;
+    static_assert(PW < NW && 64 * PW >= NMAX, "the preparing wavefront holds no tree node");
 
     __shared__ __align__(16) unsigned char smem[L::TOTAL];
     GDN_ITEM_PHASE_DECL
@@ -250,25 +252,42 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     // ------------------------------------------------ fused commit
     // One chunk of the accepted path, from root-first position c0 on, by the
     // calling wavefront: K rows into CK, G and beta, X, then T' (hi, lo).
-    auto commit_prep = [&](int c0) __attribute__((always_inline)) {
+    // Its global loads (the chunk's K rows, g and beta of its nodes), issued
+    // ahead of the rest so that their latency passes in other work.
+    constexpr int KL = 16 * CH / 64;   // 16-byte pieces of the chunk's K rows per lane
+    static_assert(KL * 64 == 16 * CH, "K pieces per lane");
+    struct PrepLoads {
+        uint4 k[KL];
+        float g, beta;
+    };
+    auto commit_load = [&](int c0) __attribute__((always_inline)) -> PrepLoads {
+        PrepLoads r;
         const int m = cmisc[0];
         const int n = min(m - c0, 16);
         const uint16_t* kp = static_cast<const uint16_t*>(c.k);
-        for (int e = lane; e < 16 * CH; e += 64) {
+#pragma unroll
+        for (int q = 0; q < KL; ++q) {
+            const int e = lane + 64 * q;
             const int t = e / CH, ch = e % CH;
-            uint4 val = make_uint4(0u, 0u, 0u, 0u);
-            if (t < n) {
-                const int node = cpath[m - 1 - (c0 + t)];
-                val = *reinterpret_cast<const uint4*>(kp + ((static_cast<size_t>(b) * N + node) * Hk + kh) * DK + 8 * ch);
-            }
-            put_chunk_at(CKb, t, ch, val, 0xFFFFFFFFu);
+            const int node = cpath[m - 1 - (c0 + min(t, n - 1))];
+            r.k[q] = *reinterpret_cast<const uint4*>(kp + ((static_cast<size_t>(b) * N + node) * Hk + kh) * DK + 8 * ch);
         }
-        float G = 0.f, bt = 0.f;
-        if (lane < n) {
-            const size_t nh = (static_cast<size_t>(b) * N + cpath[m - 1 - (c0 + lane)]) * Hv + h;
-            G = c.g[nh];
-            bt = c.beta[nh];
+        const size_t nh = (static_cast<size_t>(b) * N + cpath[m - 1 - (c0 + min(lane & 15, n - 1))]) * Hv + h;
+        r.g = c.g[nh];
+        r.beta = c.beta[nh];
+        return r;
+    };
+    auto commit_prep_rest = [&](int c0, const PrepLoads& r) __attribute__((always_inline)) {
+        const int m = cmisc[0];
+        const int n = min(m - c0, 16);
+#pragma unroll
+        for (int q = 0; q < KL; ++q) {
+            const int e = lane + 64 * q;
+            const int t = e / CH, ch = e % CH;
+            put_chunk_at(CKb, t, ch, r.k[q], t < n ? 0xFFFFFFFFu : 0u);
         }
+        float G = lane < n ? r.g : 0.f;
+        const float bt = lane < n ? r.beta : 0.f;
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) {
             const float x = __shfl_up(G, o, 16);
@@ -332,6 +351,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
             }
         }
     };
+    auto commit_prep = [&](int c0) __attribute__((always_inline)) { commit_prep_rest(c0, commit_load(c0)); };
     // The prepared chunk from root-first position c0 applied to this
     // wavefront's 16 state rows s0 (the layout of s0r below); cvr: this
     // lane's piece of the chunk's V row lc (value columns col0 + 4 lg .. + 3)
@@ -526,11 +546,15 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
 #pragma unroll
         for (int w = 0; w < L::AW; ++w) anc[i * L::AW + w] = bits[w];
     }
+    // fused commit: one lane of the preparing wavefront walks the accepted
+    // path
     if constexpr (CMT) {
-        if (tid == 64 * PW) {
-            int mm = 0;
-            for (int s = cmisc[1]; s >= 0; s = cpar[s]) cpath[mm++] = static_cast<uint8_t>(s);
-            cmisc[0] = mm;
+        if (wave == PW) {
+            if (lane == 0) {
+                int mm = 0;
+                for (int s = cmisc[1]; s >= 0; s = cpar[s]) cpath[mm++] = static_cast<uint8_t>(s);
+                cmisc[0] = mm;
+            }
         }
     }
     __syncthreads();
@@ -621,12 +645,24 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
             }
         }
     }
+    // fused commit: the loads of the path's first chunk, issued once this
+    // wavefront's (light) share of the Gram is done, arrive during the
+    // barrier and the next phase
+    PrepLoads pl{};
+    if constexpr (CMT) {
+        if (wave == PW && cmisc[0] > 0) pl = commit_load(0);
+    }
     __syncthreads();
 
     // ------------------------------------------------ (4) X, Y
     // each node's row: X_{i, t_d} = beta_i D_{i, t_d} (k_i . k_{t_d}) for the
     // ancestor t_d at distance d >= 1, Y_{i, t_d} for d >= 0 (zero past the root)
     GDN_ITEM_PHASE(3);
+    // fused commit: the first chunk's T' by the preparing wavefront, which
+    // holds no node
+    if constexpr (CMT) {
+        if (wave == PW && cmisc[0] > 0) commit_prep_rest(0, pl);
+    }
     // the path of this thread's node, four node indices (bytes) per register
     uint32_t ttp[ZR / 4];
     auto tt = [&](int d) -> int { return static_cast<int>((ttp[d >> 2] >> (8 * (d & 3))) & 0xFFu); };
@@ -662,9 +698,6 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     // where X_{p_d, p_e} sits at slot e - d of row p_d; y_d = D_{i, p_d}
     // (q_i . k_{p_d}); the scaling z_d *= beta_{p_d} follows in (6)
     GDN_ITEM_PHASE(4);
-    if constexpr (CMT) {
-        if (wave == PW && cmisc[0] > 0) commit_prep(0);
-    }
     float z[ZR];
     if (tid < N) {
         const int i = tid;
