@@ -106,10 +106,9 @@ def read_traffic(kernel, workload=WORKLOAD):
 
 
 COPY_CALLS = 5
-# kernel-name patterns per role; the fused kernel is the item kernel's
-# commit instantiation (template flag true)
+# kernel-name patterns per role
 KERNELS = {"verify": ("verify_ws_kernel", "verify_fast_kernel"), "commit": ("commit_mfma_kernel",),
-           "commit_verify": ("verify_item_kernel",), "copy": ("MulFunctor",)}
+           "commit_verify": ("commit_verify_kernel",), "copy": ("MulFunctor",)}
 
 
 def write_traffic(fetch_csv, write_csv, copy_mib, workload):

@@ -1,4 +1,6 @@
-// gdn_fast.hip -- MFMA tree verification for bf16 q/k/v on gfx950.
+// gdn_fast.hip -- MFMA tree verification for bf16 q/k/v and trees of 129 to
+// 256 nodes on gfx950 (smaller trees go to gdn_verify_ws.hip), and the
+// verify dispatch.
 //
 // What is computed (Trees from Marginals technical summary, Methodology,
 // "3. Rollback-Free Tree Verification for GDN"): with the tree sorted
@@ -18,25 +20,22 @@
 // Work decomposition: a persistent grid, one workgroup per compute unit,
 // each walking a contiguous run of (sequence, value head) items in head
 // order.  Consecutive items of one sequence share the tree structure
-// (depth, root paths, ancestor bits); the value heads of one key head also
-// share the staged K and Q and their Gram values.  d_v/16 wavefronts; the
-// wavefront w owns value columns [16w, 16w + 16) (one MFMA tile) and keeps
-// its slice of S0 (as a bf16 hi + lo pair) and R' in registers.  Dense
-// contractions run on v_mfma_f32_16x16x32_bf16: q and k are exact bf16; S0,
-// R' and Z~ are split into hi + lo bf16 so products stay near fp32 accuracy.
+// (depth, root paths, ancestor bits).  d_v/16 wavefronts; the wavefront w
+// owns value columns [16w, 16w + 16) (one MFMA tile) and keeps its slice of
+// S0 (as a bf16 hi + lo pair) and R' in registers.  Dense contractions run on
+// v_mfma_f32_16x16x32_bf16: q and k are exact bf16; S0, R' and Z~ are split
+// into hi + lo bf16 so products stay near fp32 accuracy.
 //
 // Per item: (1) S0 and V loads for this item are issued first, and the node
-// scalars and K/Q of the next item are prefetched into registers during this
-// one, so the memory system is not idle between items; (2) for a new
-// sequence: depth and root paths (pointer jumping, prefix sum), ancestor
-// bits; (3) for a new key head: K, Q into LDS and the Gram values of the
-// ancestor pairs (MFMA over the lower 16x16 tiles holding pairs); (4) G,
-// gamma, X, Y, the rows of Z~ (one thread per node) scattered into ready
-// MFMA A fragments; (5) per wavefront: K S0^T -> R', then per 16-row tile
-// Q S0^T and Z~ R' -> o (for trees over 128 nodes as the transposed tile,
-// S0 Q^T + R'^T Z~^T, so that each lane stores 16 contiguous bytes of o).
-// Rows of Z~ are solved in registers for paths of up to 16 nodes, or 24
-// for trees over 128 nodes.
+// scalars of the next item are prefetched into registers during this one;
+// (2) for a new sequence: depth and root paths (pointer jumping, prefix
+// sum), ancestor bits; (3) for a new key head, K into LDS; the Gram values
+// of the ancestor pairs (MFMA over the lower 16x16 tiles holding pairs, Q
+// rows read per row tile); (4) G, gamma, X, Y, the rows of Z~ (one thread
+// per node, in registers for paths of up to 24 nodes); (5) per wavefront:
+// K S0^T -> R', then per 16-row tile, with that tile's Q rows and Z~ blocks
+// staged in LDS by the workgroup, the transposed tile S0 Q^T + R'^T Z~^T, so
+// that each lane stores 16 contiguous bytes of o.
 //
 // Trees whose pair list exceeds the LDS budget are verified, inside the same
 // workgroup, by the per-node walk of gdn_walk.h.
@@ -62,35 +61,19 @@ namespace {
 
 __device__ __forceinline__ uint4 mask4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
 
-// Number of 16x32 blocks of Z~ for the first I row tiles: row tile I has
-// floor(I/2) + 1 blocks (k-steps of 32 nodes up to its diagonal).
-__host__ __device__ constexpr int zblocks_before(int I) {
-    return (I & 1) ? ((I + 1) / 2) * ((I + 1) / 2) : (I / 2) * (I / 2 + 1);
-}
-
-// LDS layout (bytes) for trees of at most NMAX nodes.  For NMAX <= 128
-// (DENSE) Q is staged next to K and Z~ is stored as ready-made MFMA A
-// fragments; for larger trees Q is read from global memory and the
-// fragments are built from the pair list.
+// LDS layout (bytes) for trees of at most NMAX = 256 nodes: K staged; Q read
+// from global memory per row tile (Gram) and staged per output tile; the
+// Gram values of the pairs computed per value head in place of X and Y.
 template <int NMAX, int DK>
 struct Lds {
-    static constexpr bool DENSE = NMAX <= 128;
-    // pair-list capacity: every tree of N <= 64 fits; N <= 128 covers depth
-    // <= 16 everywhere, N <= 256 depth <= 24
-    static constexpr int CAP = NMAX <= 64 ? NMAX * (NMAX + 1) / 2 : (NMAX <= 128 ? 2048 : 6144);
+    static_assert(NMAX == 256, "trees of 129 to 256 nodes");
+    // pair-list capacity: every tree of depth <= 24
+    static constexpr int CAP = 6144;
     static constexpr int AW = NMAX / 32;        // ancestor bit-row words
     static constexpr int KROW = DK * 2 + 16;    // staged k / q row, padded against bank conflicts
     static constexpr int KS_OFF = 0;
-    static constexpr int QS_OFF = NMAX * KROW;
-    static constexpr int ZD = QS_OFF + (DENSE ? NMAX * KROW : 0);  // Z~ fragment blocks (hi 1 KiB + lo 1 KiB)
-    static constexpr int ZD_BYTES = DENSE ? 2048 * zblocks_before(NMAX / 16) : 0;
-    // For NMAX <= 128 the Gram values of a key head are kept for its other
-    // value heads; larger trees recompute them per value head in place.
-    static constexpr bool KEEP_GRAM = DENSE;
-    static constexpr int KK = ZD + ZD_BYTES;    // float[CAP]: k_i . k_s of every pair (per key head)
-    static constexpr int QK = KK + (KEEP_GRAM ? 4 * CAP : 0);  // float[CAP]: q_i . k_s
-    static constexpr int XC = QK + (KEEP_GRAM ? 4 * CAP : 0);  // float[CAP]: X (per value head)
-    static constexpr int YC = XC + 4 * (CAP + 32);  // float[CAP]: Y, then the rows of Z~ (X has 32 zero pads)
+    static constexpr int XC = NMAX * KROW;      // float[CAP]: k_i . k_s, then X (per value head)
+    static constexpr int YC = XC + 4 * (CAP + 32);  // float[CAP]: q_i . k_s, then Y, then the rows of Z~ (X has 32 zero pads)
     static constexpr int PATH = YC + 4 * CAP;   // uint8[CAP]: root..i path of every node
     static constexpr int PNODE = PATH + CAP;    // uint8[CAP]: node owning each pair
     static constexpr int NODE = (PNODE + CAP + 15) & ~15;
@@ -106,9 +89,9 @@ struct Lds {
     static constexpr int TMASK = ANC + 4 * AW * NMAX;  // uint32[NMAX/16]: tile (I, J) has pairs
     static constexpr int MISC = TMASK + 4 * (NMAX / 16);
     static constexpr int FBKQ = MISC + 64;      // float[2*DK] for the fallback walk
-    // larger trees: the Q rows of one 16-row tile, staged per output tile
+    // the Q rows of one 16-row tile, staged per output tile
     static constexpr int QT = FBKQ + 8 * DK;
-    static constexpr int TOTAL = QT + (DENSE ? 0 : 16 * KROW);
+    static constexpr int TOTAL = QT + 16 * KROW;
     static_assert(NMAX * 64 * 4 + DK * 64 * 4 <= NODE, "fallback u and S0 buffers must fit below the node arrays");
 };
 
@@ -118,7 +101,6 @@ struct Lds {
 template <int NMAX, int DK, int DV, int NW>
 __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int items_per_wg) {
     using L = Lds<NMAX, DK>;
-    constexpr bool DENSE = L::DENSE;
     constexpr int NTH = 64 * NW;        // threads
     constexpr int CT = DV / (16 * NW);  // 16-column MFMA tiles per wavefront
     static_assert(CT == 1 || CT == 2, "one or two column tiles per wavefront");
@@ -163,20 +145,18 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
     int* misc = reinterpret_cast<int*>(smem + L::MISC);
     float* xc = reinterpret_cast<float*>(smem + L::XC);
     float* yc = reinterpret_cast<float*>(smem + L::YC);
-    float* kk = L::KEEP_GRAM ? reinterpret_cast<float*>(smem + L::KK) : xc;
-    float* qk = L::KEEP_GRAM ? reinterpret_cast<float*>(smem + L::QK) : yc;
+    float* kk = xc;   // the Gram values, turned into X and Y in place
+    float* qk = yc;
     uint8_t* pathc = smem + L::PATH;
     uint8_t* pnode = smem + L::PNODE;
     unsigned char* Ks = smem + L::KS_OFF;
-    unsigned char* Qs = smem + L::QS_OFF;
-    unsigned char* Zd = smem + L::ZD;
 
-    // Prefetched state of the next item: node scalars, and K/Q shares when
-    // it starts a new key head.  Loads are unconditional with indices
-    // clamped into range; out-of-range values are replaced after arrival.
+    // Prefetched state of the next item: node scalars, and the K share of a
+    // new key head.  Loads are unconditional with indices clamped into range;
+    // out-of-range values are replaced after arrival.
     int p_pf[IPT];
     float g_pf[IPT], b_pf[IPT];
-    uint4 k_pf[KCH], q_pf[DENSE ? KCH : 1];
+    uint4 k_pf[KCH];
     auto prefetch_scalars = [&](int it, int tid, int N) {
         const int bb = it / Hv, hh = it % Hv;
 #pragma unroll
@@ -196,7 +176,6 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
             const int row = min(e / (DK / 8), N - 1);
             const size_t gofs = ((static_cast<size_t>(bb) * N + row) * Hk + kh) * DK + (e % (DK / 8)) * 8;
             k_pf[q] = *reinterpret_cast<const uint4*>(kg + gofs);
-            if (DENSE) q_pf[q] = *reinterpret_cast<const uint4*>(qg + gofs);
         }
     };
     GDN_PHASE_INIT;
@@ -204,9 +183,8 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
     __builtin_amdgcn_sched_barrier(0);
     prefetch_kq(it_begin, tid0, N0);
 
-    // k_pf/q_pf hold the K/Q of the first item; afterwards the K/Q of the
-    // next item are written into LDS at the end of the current one
-    bool kq_staged = false;
+    // k_pf holds the K of the first item; a later key head's K is loaded at
+    // the start of its first item
     int cur_b = -1, cur_kh = -1, total = 0;
     for (int it = it_begin; it < it_end; ++it) {
         // Opaque copies of the thread index and N: everything derived from
@@ -223,9 +201,7 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
         const int b = it / Hv, h = it % Hv, kh = h / R;
         const bool new_b = b != cur_b;
         const bool new_kh = new_b || kh != cur_kh;
-        const bool do_gram = new_kh || !L::KEEP_GRAM;
         const int nit = it + 1 < it_end ? it + 1 : -1;
-        const bool next_new_kh = nit >= 0 && (nit / Hv != b || (nit % Hv) / R != kh);
         GDN_PHASE(0);
 
         // ---- (1) this item's S0 rows (lane (lc, lg) of tile st holds d_k
@@ -269,8 +245,6 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
                 }
             }
         }
-        if (DENSE)
-            for (int e = tid; e < L::ZD_BYTES / 16; e += NTH) reinterpret_cast<uint4*>(Zd)[e] = make_uint4(0u, 0u, 0u, 0u);
         if (nit >= 0) prefetch_scalars(nit, tid, N);
         if (new_b) {
             if (tid < NMAX / 16) tmask[tid] = 0u;
@@ -367,8 +341,6 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
                 for (int c0 = 0; c0 < DV; c0 += 64)
                     walk_verify_slice_lds<uint16_t, DK, WaveSync>(a, b, h, c0, par, u_s, Gs, ki, ki + DK, s0_s);
             }
-            if (next_new_kh) prefetch_kq(nit, tid, N);
-            kq_staged = false;
             cur_b = b;
             cur_kh = -1;
             // this path leaves the S0 and V loads above unused: drain them
@@ -384,7 +356,6 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
         // of the ancestor pairs
         const int NT = (N + 15) >> 4;
         auto q_frag = [&](int row, int ks) -> bf16x8 {
-            if (DENSE) return load_frag(Qs + row * L::KROW + 2 * (8 * KS * lg + 8 * ks));
             return load_frag(qg + ((static_cast<size_t>(b) * N + min(row, N - 1)) * Hk + kh) * DK + 8 * KS * lg + 8 * ks);
         };
         auto k_frag = [&](int row, int ks) -> bf16x8 { return load_frag(Ks + row * L::KROW + 2 * (8 * KS * lg + 8 * ks)); };
@@ -396,11 +367,10 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
                 const int cc = e % (DK / 8);
                 const uint32_t keep = row < N ? 0xFFFFFFFFu : 0u;
                 *reinterpret_cast<uint4*>(Ks + row * L::KROW + cc * 16) = mask4(k_pf[q], keep);
-                if (DENSE) *reinterpret_cast<uint4*>(Qs + row * L::KROW + cc * 16) = mask4(q_pf[q], keep);
             }
         };
-        if (new_kh && !kq_staged) {
-            if (!DENSE && it != it_begin) prefetch_kq(it, tid, N);
+        if (new_kh) {
+            if (it != it_begin) prefetch_kq(it, tid, N);
             stage_kq();
             __syncthreads();
         }
@@ -434,49 +404,32 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
                         }
                     }
         };
-        if (do_gram) {
-            if constexpr (DENSE) {
-                // lower 16x16 tiles holding pairs, dealt round-robin to the
-                // wavefronts
-                int t = 0;
-                for (int I = 0; I < NT; ++I) {
-                    const uint32_t tm = tmask[I];
-                    bf16x8 qa[KS];
+        {
+            // Q rows from global memory: each wavefront takes whole row tiles, whose
+            // Q rows it loads once, the next row tile's while it works on
+            // this one (rows w, 7 - w, 8 + w, 15 - w balance the triangle)
+            // (NTMAX / NW row tiles per wavefront, in pairs w, 2 NW - 1 - w)
+            constexpr int RU = NTMAX / NW;
+            static_assert(RU % 2 == 0 && RU * NW == NTMAX, "row-tile assignment");
+            auto row_tile = [&](int u) { return (u & 1) ? 2 * NW * (u >> 1) + 2 * NW - 1 - wave : 2 * NW * (u >> 1) + wave; };
+            bf16x8 qa[KS], qn[KS];
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) qa[ks] = q_frag(16 * I + lc, ks);
-                    for (int J = 0; J <= I; ++J) {
-                        if (!((tm >> J) & 1u)) continue;
-                        if (t++ % NW != wave) continue;
-                        gram_tile(I, J, qa);
-                    }
+            for (int ks = 0; ks < KS; ++ks) qa[ks] = q_frag(16 * row_tile(0) + lc, ks);
+#pragma unroll
+            for (int u = 0; u < RU; ++u) {
+                const int I = row_tile(u);
+                if (u + 1 < RU) {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) qn[ks] = q_frag(16 * row_tile(u + 1) + lc, ks);
                 }
-            } else {
-                // Q is not staged: each wavefront takes whole row tiles, whose
-                // Q rows it loads once, the next row tile's while it works on
-                // this one (rows w, 7 - w, 8 + w, 15 - w balance the triangle)
-                // (NTMAX / NW row tiles per wavefront, in pairs w, 2 NW - 1 - w)
-                constexpr int RU = NTMAX / NW;
-                static_assert(RU % 2 == 0 && RU * NW == NTMAX, "row-tile assignment");
-                auto row_tile = [&](int u) { return (u & 1) ? 2 * NW * (u >> 1) + 2 * NW - 1 - wave : 2 * NW * (u >> 1) + wave; };
-                bf16x8 qa[KS], qn[KS];
+                if (I < NT) {
+                    const uint32_t tm = tmask[I];
+                    for (int J = 0; J <= I; ++J)
+                        if ((tm >> J) & 1u) gram_tile(I, J, qa);
+                }
+                if (u + 1 < RU) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) qa[ks] = q_frag(16 * row_tile(0) + lc, ks);
-#pragma unroll
-                for (int u = 0; u < RU; ++u) {
-                    const int I = row_tile(u);
-                    if (u + 1 < RU) {
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) qn[ks] = q_frag(16 * row_tile(u + 1) + lc, ks);
-                    }
-                    if (I < NT) {
-                        const uint32_t tm = tmask[I];
-                        for (int J = 0; J <= I; ++J)
-                            if ((tm >> J) & 1u) gram_tile(I, J, qa);
-                    }
-                    if (u + 1 < RU) {
-#pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) qa[ks] = qn[ks];
-                    }
+                    for (int ks = 0; ks < KS; ++ks) qa[ks] = qn[ks];
                 }
             }
         }
@@ -547,27 +500,9 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
                 }
 #pragma unroll
                 for (int bb = 0; bb < ZR; ++bb) z[bb] *= bet[t[bb]];
-                if (DENSE) {
-                    // block (I, kap) = rows 16I.., nodes 32kap..; node t sits in
-                    // lane group ((t >> 2) & 3), slot 4 ((t >> 4) & 1) + (t & 3)
-                    unsigned char* rowblk = Zd + 2048 * zblocks_before(i >> 4);
 #pragma unroll
-                    for (int bb = 0; bb < ZR; ++bb) {
-                        if (bb < m) {
-                            const int tt = t[bb];
-                            const __bf16 zh = static_cast<__bf16>(z[bb]);
-                            const __bf16 zl = static_cast<__bf16>(z[bb] - static_cast<float>(zh));
-                            const int e = (((((tt >> 2) & 3) << 4) | (i & 15)) << 3) + (((tt >> 4) & 1) << 2) + (tt & 3);
-                            unsigned char* blk = rowblk + 2048 * (tt >> 5);
-                            reinterpret_cast<__bf16*>(blk)[e] = zh;
-                            reinterpret_cast<__bf16*>(blk + 1024)[e] = zl;
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int bb = 0; bb < ZR; ++bb)
-                        if (bb < m) yc[o + bb] = z[bb];
-                }
+                for (int bb = 0; bb < ZR; ++bb)
+                    if (bb < m) yc[o + bb] = z[bb];
                 continue;
             }
             for (int aa = m - 1; aa >= 1; --aa) {
@@ -576,19 +511,6 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
                 for (int bb = 0; bb < aa; ++bb) yc[o + bb] -= za * xc[oa + bb];
             }
             for (int bb = 0; bb < m; ++bb) yc[o + bb] *= bet[pathc[o + bb]];
-            if (DENSE) {
-                unsigned char* rowblk = Zd + 2048 * zblocks_before(i >> 4);
-                for (int bb = 0; bb < m; ++bb) {
-                    const int tt = pathc[o + bb];
-                    const float zz = yc[o + bb];
-                    const __bf16 zh = static_cast<__bf16>(zz);
-                    const __bf16 zl = static_cast<__bf16>(zz - static_cast<float>(zh));
-                    const int e = (((((tt >> 2) & 3) << 4) | (i & 15)) << 3) + (((tt >> 4) & 1) << 2) + (tt & 3);
-                    unsigned char* blk = rowblk + 2048 * (tt >> 5);
-                    reinterpret_cast<__bf16*>(blk)[e] = zh;
-                    reinterpret_cast<__bf16*>(blk + 1024)[e] = zl;
-                }
-            }
         }
         __syncthreads();
         GDN_PHASE(3);
@@ -620,47 +542,10 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
 #pragma unroll
             for (int st = 0; st < CT; ++st) out[st] = ah[st] + al[st];
         };
-        // gamma o (Q S0^T) of tile I
-        auto qs0 = [&](int I, f32x4 (&out)[CT]) {
-            f32x4 ah[CT], al[CT];
-#pragma unroll
-            for (int st = 0; st < CT; ++st) ah[st] = al[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 qa = q_frag(16 * I + lc, ks);
-#pragma unroll
-                for (int st = 0; st < CT; ++st) {
-                    ah[st] = mfma(qa, s0h[st][ks], ah[st]);
-                    al[st] = mfma(qa, s0l[st][ks], al[st]);
-                }
-            }
-#pragma unroll
-            for (int st = 0; st < CT; ++st)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) out[st][rr] = (ah[st][rr] + al[st][rr]) * gam[16 * I + 4 * lg + rr];
-        };
 
-        // For DENSE every tile's K S0^T and Q S0^T are taken now, which frees
-        // the staged K/Q: the next item's K/Q are prefetched into registers
-        // here and written to LDS at the end of this item.
-        constexpr int PT = DENSE ? NTMAX : 1;
-        f32x4 pk[PT][CT], pq[PT][CT];
-        if constexpr (DENSE) {
-#pragma unroll
-            for (int S = 0; S < NTMAX; ++S) {
-                if (S < NT) {
-                    ks0(S, pk[S]);
-                    qs0(S, pq[S]);
-                } else {
-#pragma unroll
-                    for (int st = 0; st < CT; ++st) pk[S][st] = pq[S][st] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-            }
-        }
         GDN_PHASE(4);
-        // (larger trees load the next key head's K at the start of its item:
-        // held here, those registers would spill R')
-        if (DENSE && next_new_kh) prefetch_kq(nit, tid, N);
+        // (the next key head's K is loaded at the start of its item: held
+        // here, those registers would spill R')
 
         // R' = V - gamma o (K S0^T) as MFMA fragments (k = node) of the Z~ R' product:
         // k-step kap covers nodes [32 kap, 32 kap + 32); lane (lc, lg) holds
@@ -673,16 +558,11 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
             for (int half = 0; half < 2; ++half) {
                 const int S = 2 * kap + half;
                 f32x4 pks[CT];
-                if constexpr (DENSE) {
-#pragma unroll
-                    for (int st = 0; st < CT; ++st) pks[st] = pk[S][st];
+                if (S < NT) {
+                    ks0(S, pks);
                 } else {
-                    if (S < NT) {
-                        ks0(S, pks);
-                    } else {
 #pragma unroll
-                        for (int st = 0; st < CT; ++st) pks[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
+                    for (int st = 0; st < CT; ++st) pks[st] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
@@ -702,43 +582,7 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
 
         GDN_PHASE(5);
         // O tiles: gamma o (Q S0^T) + Z~ R'
-        const size_t obase = static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV + column(0);
-        auto store_tile = [&](int I, const f32x4 (&acc)[CT]) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int i = 16 * I + 4 * lg + rr;
-                if (i < N) {
-                    float* orow = a.o + obase + static_cast<size_t>(i) * Hv * DV;
-                    if (CT == 1)
-                        *orow = acc[0][rr];
-                    else
-                        *reinterpret_cast<float2*>(orow) = make_float2(acc[0][rr], acc[CT - 1][rr]);
-                }
-            }
-        };
-        if constexpr (DENSE) {
-#pragma unroll
-            for (int I = 0; I < NTMAX; ++I) {
-                if (I < NT) {
-                    f32x4 acc[CT];
-#pragma unroll
-                    for (int st = 0; st < CT; ++st) acc[st] = pq[I][st];
-                    const unsigned char* blk = Zd + 2048 * zblocks_before(I) + 16 * lane;
-#pragma unroll
-                    for (int kap = 0; kap <= I / 2; ++kap) {
-                        const bf16x8 zh = load_frag(blk + 2048 * kap);
-                        const bf16x8 zl = load_frag(blk + 2048 * kap + 1024);
-#pragma unroll
-                        for (int st = 0; st < CT; ++st) {
-                            acc[st] = mfma(zh, rh[st][kap], acc[st]);
-                            acc[st] = mfma(zh, rl[st][kap], acc[st]);
-                            acc[st] = mfma(zl, rh[st][kap], acc[st]);
-                        }
-                    }
-                    store_tile(I, acc);
-                }
-            }
-        } else {
+        {
             // per 16-row tile: its Q rows and its row blocks of Z~ (from the
             // pair list, in the X area, free after the solve) staged in LDS
             // by the whole workgroup, then each wavefront's columns
@@ -824,12 +668,6 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
         GDN_PHASE(6);
         cur_b = b;
         cur_kh = kh;
-        // DENSE: the staged K/Q are no longer read; put the next item's there
-        kq_staged = DENSE && next_new_kh;
-        if (kq_staged) {
-            __syncthreads();
-            stage_kq();
-        }
         __syncthreads();  // the next item rewrites LDS
         GDN_PHASE(7);
     }

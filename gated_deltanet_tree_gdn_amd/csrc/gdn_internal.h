@@ -67,10 +67,8 @@ struct CommitPrev {
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // The MFMA verify for bf16 and N <= 128.
 hipError_t launch_verify_ws(const VerifyArgs& a, hipStream_t stream);
-// Item-per-workgroup MFMA verify (bf16, N <= 128); not dispatched by
-// launch_verify.  With a CommitPrev it first commits the previous tree's
-// accepted path into c.S_next (== a.S0) and verifies on that state.
-hipError_t launch_verify_item(const VerifyArgs& a, hipStream_t stream);
+// The commit of the previous tree's accepted path into c.S_next (== a.S0)
+// fused into the verify of the tree in `a` (bf16, N <= 128).
 hipError_t launch_commit_verify(const VerifyArgs& a, const CommitPrev& c, hipStream_t stream);
 // Per-branch recurrent verification (the comparison baseline).
 hipError_t launch_verify_branches(const VerifyArgs& a, hipStream_t stream);

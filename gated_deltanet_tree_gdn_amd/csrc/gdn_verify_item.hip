@@ -1,6 +1,7 @@
-// gdn_verify_item.hip -- MFMA tree verification for bf16 q/k/v and trees of
-// at most 128 nodes on gfx950, one (sequence, value head) item per
-// workgroup, several workgroups resident per compute unit.
+// gdn_verify_item.hip -- the delayed commit fused into the next tree's
+// verification (gdn_commit_verify) for bf16 q/k/v and trees of at most 128
+// nodes on gfx950: one (sequence, value head) item per workgroup, two
+// workgroups resident per compute unit.
 //
 // What is computed (Trees from Marginals technical summary, Methodology,
 // "3. Rollback-Free Tree Verification for GDN"): over the ancestor pairs of
@@ -13,12 +14,11 @@
 //     O = gamma o (Q S0^T) + Z~ R'.
 // Row i of Z~ is found by back-substitution along the root-to-i path.
 //
-// Why one item per workgroup: the path is bound by HBM traffic (S0, V and
-// K/Q in, o out), and a compute unit keeps its memory pipe full only when
-// the loads of one item overlap the MFMA work and stores of another.  Two
-// independent workgroups per compute unit, each taking one item through its
-// phases in order, give that overlap without any hand-over protocol; the LDS
-// budget (at most 80 KB each) is what fixes the layout:
+// One item per workgroup, two independent workgroups per compute unit, each
+// taking one item through its phases in order: the loads of one can overlap
+// the MFMA work and stores of the other without any hand-over protocol, and
+// the LDS of one workgroup (at most 80 KB) leaves room for the commit's
+// chunk, which the persistent verify kernel's does not.  The layout:
 //   - one 32 KB buffer holds K (for the Gram and K S0^T), then Q (for
 //     Q S0^T), in the MFMA k-slot order with chunks XOR-swizzled by row;
 //   - one 40 KB area holds the tree arrays (pair lists of k.k, q.k and X,
@@ -39,7 +39,7 @@
 // Trees with a root path longer than 16 nodes, or more ancestor pairs than
 // the area holds, are verified by the per-node walk of gdn_walk.h.
 //
-// Fused commit (CMT): the delayed state commitment of the previous tree
+// The commit: the delayed state commitment of the previous tree
 // (same page, section 3: the state is committed once the accepted branch is
 // known, at the next decoding step) runs inside the next tree's verify, so
 // the committed state is formed in registers, written once, and used by
@@ -50,10 +50,11 @@
 //     T' = diag(D_{n-1, .}) (I + X)^-1 diag(beta)   (n nodes in the chunk),
 //     S <- gamma_{n-1} S + K^T T' (V - gamma o (K S^T)),
 // which is the GDN delta rule applied node by node along the chunk.  One
-// otherwise idle wavefront walks the accepted path, stages the chunk's K
-// rows, and forms T' (16 lanes, one column each, by forward substitution)
-// while the tree is solved; every wavefront then applies the chunk to its
-// own 16 state rows on MFMA (K S^T with S as bf16 hi + lo, T' and the
+// wavefront that holds no tree node walks the accepted path, loads the
+// chunk's K rows, g and beta once its Gram tiles are done, and forms X and T'
+// (16 lanes, one column each, by forward substitution) in the X/Y phase;
+// after the Z~ scatter every wavefront applies the chunk to its own 16 state
+// rows on MFMA (K S^T with S as bf16 hi + lo, T' and the
 // right-hand side as hi + lo, K^T from K by transposing MFMAs against the
 // identity).
 
@@ -82,7 +83,7 @@ __host__ __device__ constexpr int vi_zblocks(int I) {
 __host__ __device__ constexpr int vi_align(int x, int a) { return (x + a - 1) / a * a; }
 __host__ __device__ constexpr int vi_max(int x, int y) { return x > y ? x : y; }
 
-template <int NMAX, int DK, int DV, bool CMT>
+template <int NMAX, int DK, int DV>
 struct ItemLds {
     static constexpr int NTMAX = NMAX / 16;
     static constexpr int AW = NMAX / 32;
@@ -126,15 +127,15 @@ struct ItemLds {
     static constexpr int CPAR = CB + 64;               // int8[NMAX]: parents of the previous tree
     static constexpr int CPATH = CPAR + NMAX;          // uint8[NMAX]: accepted .. root
     static constexpr int CMISC = CPATH + NMAX;         // int[4]: 0 path length, 1 accepted node
-    static constexpr int TOTAL = CMT ? CMISC + 16 : MISC + 64;
+    static constexpr int TOTAL = CMISC + 16;
     static_assert(TOTAL <= 80 * 1024, "two workgroups per compute unit");
-    static_assert(!CMT || NMAX <= 128, "parents of the previous tree as int8");
+    static_assert(NMAX <= 128, "parents of the previous tree as int8");
     // misc[]: 1 a path longer than ZR (1), 2 an invalid parent (1)
 };
 
-template <int NMAX, int DK, int DV, bool CMT>
-__global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(VerifyArgs a, CommitPrev c) {
-    using L = ItemLds<NMAX, DK, DV, CMT>;
+template <int NMAX, int DK, int DV>
+__global__ __launch_bounds__(4 * DV, 4 * DV / 128) void commit_verify_kernel(VerifyArgs a, CommitPrev c) {
+    using L = ItemLds<NMAX, DK, DV>;
     constexpr int NW = DV / 16;          // wavefronts, 16 value columns each
     constexpr int NTH = 64 * NW;
     constexpr int KS = DK / 32;
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
         gv[i] = gi;
         bet[i] = bi;
         if (tid < NTMAX) tmask[tid] = 0u;
-        if constexpr (CMT) {
+        {
             // the previous tree's parents (outside [-1, i - 1]: read as -1)
             int pp = -1;
             if (i < N) {
@@ -490,7 +491,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
             cpar[i] = static_cast<int8_t>(pp);
         }
     }
-    if constexpr (CMT) {
+    {
         if (tid == NTH - 1) {
             // an accepted node out of range is reported and read as -1
             int acc = c.accepted[b];
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     }
     // fused commit: one lane of the preparing wavefront walks the accepted
     // path
-    if constexpr (CMT) {
+    {
         if (wave == PW) {
             if (lane == 0) {
                 int mm = 0;
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     if (!fast) {
         // a path longer than ZR: the per-node walk, one wavefront per
         // 64-column slice in turn (the others have nothing to do for this item)
-        if constexpr (CMT) {
+        {
             // the committed state first: the walk reads it back from a.S0
             refresh();
             const int col = NW == 8 ? 32 * (wave & 3) + 16 * (wave >> 2) : 16 * wave;
@@ -649,7 +650,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     // wavefront's (light) share of the Gram is done, arrive during the
     // barrier and the next phase
     PrepLoads pl{};
-    if constexpr (CMT) {
+    {
         if (wave == PW && cmisc[0] > 0) pl = commit_load(0);
     }
     __syncthreads();
@@ -660,7 +661,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     GDN_ITEM_PHASE(3);
     // fused commit: the first chunk's T' by the preparing wavefront, which
     // holds no node
-    if constexpr (CMT) {
+    {
         if (wave == PW && cmisc[0] > 0) commit_prep_rest(0, pl);
     }
     // the path of this thread's node, four node indices (bytes) per register
@@ -739,14 +740,14 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     // fused commit: an accepted path of more than one chunk is applied
     // after the Z~ scatter with the V loads held back (its chunk
     // preparations run in between and need the registers)
-    const int cm = CMT ? cmisc[0] : 0;
+    const int cm = cmisc[0];
     {
         const float4* src = reinterpret_cast<const float4*>(
-            (CMT ? c.S0 : a.S0) + ((static_cast<size_t>(b) * Hv + h) * DV + col0 + lc) * DK + 4 * lg);
+            c.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + col0 + lc) * DK + 4 * lg);
 #pragma unroll
         for (int q = 0; q < 2 * KS; ++q) s0r[q] = src[4 * q];
         if (cm <= 16) load_v();
-        if constexpr (CMT) {
+        {
             if (cm > 0) cvr0 = commit_v(0, col0);
         }
     }
@@ -779,7 +780,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     s16x4 eye;
 #pragma unroll
     for (int q = 0; q < 4; ++q) eye[q] = 4 * lg + q == lc ? static_cast<short>(0x3F80) : short(0);
-    if constexpr (CMT) {
+    {
         if (cm > 16) {
             commit_all(s0r, col0, true, cvr0, eye);
             load_v();
@@ -867,8 +868,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void verify_item_kernel(Verif
     GDN_ITEM_PHASE_END;
 }
 
-template <bool CMT>
-hipError_t launch_item(const VerifyArgs& a, const CommitPrev& c, hipStream_t stream) {
+hipError_t launch_cv(const VerifyArgs& a, const CommitPrev& c, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.B) * a.H_v);
     auto go = [&](auto kern, int dv) {
         hipLaunchKernelGGL(kern, grid, dim3(4 * dv), 0, stream, a, c);
@@ -876,22 +876,18 @@ hipError_t launch_item(const VerifyArgs& a, const CommitPrev& c, hipStream_t str
     };
     if (a.N <= 64) {
         if (a.d_k == 64)
-            return a.d_v == 64 ? go(verify_item_kernel<64, 64, 64, CMT>, 64) : go(verify_item_kernel<64, 64, 128, CMT>, 128);
-        return a.d_v == 64 ? go(verify_item_kernel<64, 128, 64, CMT>, 64) : go(verify_item_kernel<64, 128, 128, CMT>, 128);
+            return a.d_v == 64 ? go(commit_verify_kernel<64, 64, 64>, 64) : go(commit_verify_kernel<64, 64, 128>, 128);
+        return a.d_v == 64 ? go(commit_verify_kernel<64, 128, 64>, 64) : go(commit_verify_kernel<64, 128, 128>, 128);
     }
     if (a.d_k == 64)
-        return a.d_v == 64 ? go(verify_item_kernel<128, 64, 64, CMT>, 64) : go(verify_item_kernel<128, 64, 128, CMT>, 128);
-    return a.d_v == 64 ? go(verify_item_kernel<128, 128, 64, CMT>, 64) : go(verify_item_kernel<128, 128, 128, CMT>, 128);
+        return a.d_v == 64 ? go(commit_verify_kernel<128, 64, 64>, 64) : go(commit_verify_kernel<128, 64, 128>, 128);
+    return a.d_v == 64 ? go(commit_verify_kernel<128, 128, 64>, 64) : go(commit_verify_kernel<128, 128, 128>, 128);
 }
 
 }  // namespace
 
-hipError_t launch_verify_item(const VerifyArgs& a, hipStream_t stream) {
-    return launch_item<false>(a, CommitPrev{}, stream);
-}
-
 hipError_t launch_commit_verify(const VerifyArgs& a, const CommitPrev& c, hipStream_t stream) {
-    return launch_item<true>(a, c, stream);
+    return launch_cv(a, c, stream);
 }
 
 }  // namespace gdn
