@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 WORKLOAD = "bestfirst_b32n128"
 KERNEL_SOURCES = ["gdn_internal.h", "gdn_mfma.h", "gdn_walk.h", "gdn_fast.hip", "gdn_verify_ws.hip",
-                  "gdn_verify_item.hip", "gdn_commit.hip"]
+                  "gdn_commit_verify.hip", "gdn_commit.hip"]
 STRESS = "stress48"
 
 

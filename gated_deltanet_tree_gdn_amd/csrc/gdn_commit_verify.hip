@@ -1,4 +1,4 @@
-// gdn_verify_item.hip -- the delayed commit fused into the next tree's
+// gdn_commit_verify.hip -- the delayed commit fused into the next tree's
 // verification (gdn_commit_verify) for bf16 q/k/v and trees of at most 128
 // nodes on gfx950: one (sequence, value head) item per workgroup, two
 // workgroups resident per compute unit.
