@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 WORKLOAD = "bestfirst_b32n128"
 KERNEL_SOURCES = ["gdn_internal.h", "gdn_mfma.h", "gdn_walk.h", "gdn_fast.hip", "gdn_verify_ws.hip",
-                  "gdn_commit_verify.hip", "gdn_commit.hip"]
+                  "gdn_split.hip", "gdn_commit_verify.hip", "gdn_commit.hip"]
 STRESS = "stress48"
 
 
@@ -106,8 +106,10 @@ def read_traffic(kernel, workload=WORKLOAD):
 
 
 COPY_CALLS = 5
-# kernel-name patterns per role
-KERNELS = {"verify": ("verify_ws_kernel", "verify_fast_kernel"), "commit": ("commit_mfma_kernel",),
+# kernel-name patterns per role; a verify of more than 128 nodes is the
+# tree kernel and then the dense kernel, whose per-launch bytes add up
+KERNELS = {"verify": ("verify_ws_kernel", "verify_fast_kernel"), "verify_tree": ("tree_kernel",),
+           "verify_dense": ("dense_kernel",), "commit": ("commit_mfma_kernel",),
            "commit_verify": ("commit_verify_kernel",), "copy": ("MulFunctor",)}
 
 
@@ -138,11 +140,15 @@ def write_traffic(fetch_csv, write_csv, copy_mib, workload):
     out = {"kernel_source_sha": kernel_source_sha(), "copy_kib": copy_kib,
            "fetch_factor": ff, "write_factor": fw, "dispatches": {"fetch": nf, "write": nw}}
     out["workload"] = workload
-    for k in ("verify", "commit", "commit_verify"):
+    for k in ("verify", "verify_tree", "verify_dense", "commit", "commit_verify"):
         if fetch[k] is None or write[k] is None:
             continue
         out[k] = {"fetch_kib": fetch[k], "write_kib": write[k],
                   "hbm_bytes_per_launch": 1024.0 * (fetch[k] * ff + write[k] * fw)}
+    if "verify" not in out and "verify_tree" in out and "verify_dense" in out:
+        out["verify"] = {k: out["verify_tree"][k] + out["verify_dense"][k]
+                         for k in ("fetch_kib", "write_kib", "hbm_bytes_per_launch")}
+        out["verify"]["kernels"] = "tree_kernel + dense_kernel"
     out["hbm_bytes_per_launch"] = out.get("verify", {}).get("hbm_bytes_per_launch")
     with open(traffic_file(workload), "w") as f:
         json.dump(out, f, indent=1)
@@ -475,6 +481,7 @@ def main():
                   "verify_us": sv_ms * 1e3, "commit_us": sc_ms * 1e3, "verify_algorithmic_bytes": sb,
                   "verify_GBps": sb / (sv_ms * 1e-3) / 1e9, "verify_frac_of_peak": sb / (sv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "verify_traffic": read_traffic("verify", STRESS),
+                  "verify_kernels": "tree_kernel, then dense_kernel (two launches over the context's workspace)",
                   "verify_nodes_heads_per_s": scfg.B * scfg.N * scfg.H_v / (sv_ms * 1e-3)}
         del ssets, sets
         torch.cuda.empty_cache()

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdn_tree.so")
 
-SOURCES = ["gdn_tree_api.cpp", "gdn_simple.hip", "gdn_fast.hip", "gdn_verify_ws.hip", "gdn_commit_verify.hip", "gdn_commit.hip", "gdn_draft.hip", "gdn_branch.hip", "gdn_static.hip"]
+SOURCES = ["gdn_tree_api.cpp", "gdn_simple.hip", "gdn_fast.hip", "gdn_verify_ws.hip", "gdn_commit_verify.hip", "gdn_commit.hip", "gdn_draft.hip", "gdn_branch.hip", "gdn_static.hip", "gdn_split.hip"]
 
 # Packed fp32 VALU ops are switched off for all device code.
 HIP_FLAGS = [

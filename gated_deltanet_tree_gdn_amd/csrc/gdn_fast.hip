@@ -1,6 +1,8 @@
-// gdn_fast.hip -- MFMA tree verification for bf16 q/k/v and trees of 129 to
-// 256 nodes on gfx950 (smaller trees go to gdn_verify_ws.hip), and the
-// verify dispatch.
+// gdn_fast.hip -- single-launch MFMA tree verification for bf16 q/k/v and
+// trees of 129 to 256 nodes on gfx950, used where no workspace is at hand
+// (the allocation-free entry point; with a context the two-launch verify of
+// gdn_split.hip runs instead, and smaller trees go to gdn_verify_ws.hip),
+// and the verify dispatch.
 //
 // What is computed (Trees from Marginals technical summary, Methodology,
 // "3. Rollback-Free Tree Verification for GDN"): with the tree sorted
@@ -711,6 +713,9 @@ hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
     // trees of up to 128 nodes: one workgroup per compute unit, tree and
     // dense parts of consecutive items overlapped on separate wavefronts
     if (a.N <= 128) return launch_verify_ws(a, stream);
+    // larger trees: the two-launch verify over the context's workspace;
+    // without one (the allocation-free entry point) this file's kernel
+    if (a.split_ws) return launch_verify_split(a, stream);
     if (a.d_k == 128) return a.d_v == 128 ? verify_fast<256, 128, 128>(a, stream) : verify_fast<256, 128, 64>(a, stream);
     return a.d_v == 128 ? verify_fast<256, 64, 128>(a, stream) : verify_fast<256, 64, 64>(a, stream);
 }

@@ -29,7 +29,57 @@ struct VerifyArgs {
     float* o;
     int32_t* tree_status;  // [B]: 0 or GDN_ERR_TREE
     int force_walk;        // 1: per-node walk even for bf16 (GDN_FORCE_SIMPLE=1)
+    void* split_ws;        // split_ws_bytes(B, N, H_v) bytes of device workspace for the
+                           // two-launch verify of N > 128, or NULL (single-launch kernels)
 };
+
+// The two-launch verify's workspace (gdn_split.hip): per (sequence, value
+// head) the pair values of Z~ and gamma, per sequence the pair structure.
+struct SplitWs {
+    float* z;        // [B][H_v][P]
+    float* gam;      // [B][H_v][N]
+    uint8_t* path;   // [B][P]: ancestor of each pair
+    uint8_t* pnode;  // [B][P]: node of each pair
+    int32_t* off;    // [B][N + 1]: first pair of each node, then the count
+    int32_t* deep;   // [B]: 1 for a root path the tree kernel does not solve
+    int P;           // pair capacity per sequence
+};
+// Byte offsets of the arrays in the workspace (each 256-aligned); pairs per
+// sequence at most N ZR, ZR the longest root path the tree kernel solves.
+struct SplitLayout {
+    size_t z, gam, path, pnode, off, deep, total;
+    int P;
+};
+inline int split_zr(int N) { return N > 128 ? 24 : 16; }
+inline SplitLayout split_layout(int B, int N, int Hv) {
+    auto r256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+    SplitLayout l{};
+    l.P = (N > 0 ? N : 1) * split_zr(N);
+    const size_t b = B > 0 ? B : 1, n = N > 0 ? N : 1, h = Hv > 0 ? Hv : 1;
+    l.z = 0;
+    l.gam = l.z + r256(b * h * l.P * sizeof(float));
+    l.path = l.gam + r256(b * h * n * sizeof(float));
+    l.pnode = l.path + r256(b * l.P);
+    l.off = l.pnode + r256(b * l.P);
+    l.deep = l.off + r256(b * (n + 1) * sizeof(int32_t));
+    l.total = l.deep + r256(b * sizeof(int32_t));
+    return l;
+}
+// Zero for trees of at most 128 nodes, which the single-launch kernel verifies.
+inline size_t split_ws_bytes(int B, int N, int Hv) { return N > 128 ? split_layout(B, N, Hv).total : 0; }
+inline SplitWs split_ws_at(void* base, int B, int N, int Hv) {
+    const SplitLayout l = split_layout(B, N, Hv);
+    unsigned char* p = static_cast<unsigned char*>(base);
+    SplitWs w;
+    w.z = reinterpret_cast<float*>(p + l.z);
+    w.gam = reinterpret_cast<float*>(p + l.gam);
+    w.path = p + l.path;
+    w.pnode = p + l.pnode;
+    w.off = reinterpret_cast<int32_t*>(p + l.off);
+    w.deep = reinterpret_cast<int32_t*>(p + l.deep);
+    w.P = l.P;
+    return w;
+}
 
 // Arguments of one accepted-path commit.
 struct CommitArgs {
@@ -67,6 +117,9 @@ struct CommitPrev {
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // The MFMA verify for bf16 and N <= 128.
 hipError_t launch_verify_ws(const VerifyArgs& a, hipStream_t stream);
+// The two-launch MFMA verify (tree kernel, then dense kernel) for bf16 and
+// 128 < N <= 256 over a.split_ws.
+hipError_t launch_verify_split(const VerifyArgs& a, hipStream_t stream);
 // The commit of the previous tree's accepted path into c.S_next (== a.S0)
 // fused into the verify of the tree in `a` (bf16, N <= 128).
 hipError_t launch_commit_verify(const VerifyArgs& a, const CommitPrev& c, hipStream_t stream);

@@ -1,0 +1,749 @@
+// gdn_split.hip -- tree verification in two launches for bf16 q/k/v and
+// trees of 129 to 256 nodes on gfx950: a tree kernel that forms, for every
+// (sequence, value head), the tree-shaped operator Z~ and gamma into the
+// context's workspace, then a dense kernel that streams S0, V, K and Q of
+// each (sequence, value head) through the MFMA contractions and writes o.
+//
+// What is computed (Trees from Marginals technical summary, Methodology,
+// "3. Rollback-Free Tree Verification for GDN"): over the ancestor pairs of
+// the topologically sorted tree,
+//     X_is = beta_i D_is (k_i . k_s)  (s a strict ancestor of i),
+//     Y_is = D_is (q_i . k_s)         (s an ancestor of i, or i),
+// (D_is = exp(G_i - G_s), G the path sum of the log-gates, gamma = exp(G)),
+// the masked triangular solve (I + X) U = diag(beta) (V - gamma o K S0^T)
+// and the output O = gamma o Q S0^T + Y U.  The solve is folded into an
+// N x N operator with the ancestor pattern of the tree, which does not
+// depend on d_v:
+//     Z~ = Y (I + X)^-1 diag(beta),  R' = V - gamma o (K S0^T),
+//     O = gamma o (Q S0^T) + Z~ R'.
+//
+// Why two launches: at this size one item's tree side (structure, Gram of
+// the ancestor pairs, X and Y, the row solve) is a long chain of dependent
+// phases, and an item's dense side needs most of a compute unit's LDS and
+// registers, so the two cannot share a workgroup without running in turn.
+// Here the tree kernel runs the chains of the whole batch side by side, one
+// workgroup per (sequence, key head) that computes the Gram once for the
+// value heads of the key head and solves two value heads at a time, and the
+// dense kernel runs one item per workgroup, two workgroups per compute unit.
+// Between them go the pair values (4 bytes per ancestor pair and value
+// head) and gamma; K and Q are read by both.  (For trees of at most 128
+// nodes the persistent single-launch kernel of gdn_verify_ws.hip, which
+// overlaps one item's tree side with another's dense side, is faster.)
+//
+// Workspace (per context, written by the tree kernel, read by the dense
+// kernel), with P = N ZR pairs per sequence at most (ZR = 16 for N <= 128,
+// 24 above):
+//   z     float [B][H_v][P]  Z~ values in pair order (below), times beta of
+//                            the ancestor
+//   gam   float [B][H_v][N]  gamma
+//   path  uint8 [B][P]       the ancestor s of each pair
+//   pnode uint8 [B][P]       the node i of each pair
+//   off   int32 [B][N + 1]   first pair of each node; off[N] = pair count
+//   deep  int32 [B]          1: a root path longer than ZR nodes (the
+//                            dense kernel walks that sequence per node)
+// Pair order: node by node; node i's pairs are its root path, root first
+// (position d holds the ancestor at depth d + 1, the last one i itself).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gdn_internal.h"
+#include "gdn_mfma.h"
+#include "gdn_walk.h"
+
+// Phase markers: no-ops here; a timing build defines them to record when
+// each phase of a workgroup starts.
+#ifndef GDN_SPLIT_PHASE
+#define GDN_SPLIT_PHASE_DECL
+#define GDN_SPLIT_PHASE(k)
+#define GDN_SPLIT_PHASE_END(kind, id)
+#endif
+
+namespace gdn {
+
+namespace {
+
+__host__ __device__ constexpr int sp_align(int x, int a) { return (x + a - 1) / a * a; }
+__host__ __device__ constexpr int sp_max(int x, int y) { return x > y ? x : y; }
+__host__ __device__ constexpr int sp_zr(int n) { return n > 128 ? 24 : 16; }
+
+
+// ---------------------------------------------------------------- tree kernel
+
+template <int NMAX, int DK>
+struct TreeLds {
+    static constexpr int ZR = sp_zr(NMAX);
+    static constexpr int CAP = NMAX * ZR;
+    static constexpr int AW = NMAX / 32;                 // ancestor bit-row words
+    static constexpr int KROW = DK * 2 + 16;             // staged k row, padded against bank conflicts
+    static constexpr int KS_BYTES = NMAX * KROW;
+    static constexpr int XH = CAP + 32;                  // X of one value head (32 zero pads)
+    static constexpr int KS = 0;                         // K rows; after the Gram, X of two value heads
+    static constexpr int KK = sp_align(sp_max(KS_BYTES, 2 * 4 * XH), 16);  // float[CAP + 4]: k_i . k_s
+    static constexpr int QK = KK + 4 * (CAP + 4);        // float[CAP + 4]: q_i . k_s
+    static constexpr int PATH = QK + 4 * (CAP + 4);      // uint8[CAP]
+    static constexpr int PNODE = PATH + CAP;             // uint8[CAP]
+    static constexpr int NODE = sp_align(PNODE + CAP, 16);
+    static constexpr int PAR = NODE;                     // int[NMAX]
+    static constexpr int DEP = PAR + 4 * NMAX;           // int[NMAX]: nodes on the root path
+    static constexpr int NXT = DEP + 4 * NMAX;           // int[NMAX]: pointer jumping
+    static constexpr int OFF = NXT + 4 * NMAX;           // int[NMAX + 16]
+    static constexpr int GV = OFF + 4 * (NMAX + 16);     // float[2][NMAX]: g of two value heads
+    static constexpr int BET = GV + 8 * NMAX;            // float[2][NMAX]: beta
+    static constexpr int GG = BET + 8 * NMAX;            // float[2][NMAX]: G
+    static constexpr int ANC = GG + 8 * NMAX;            // uint32[NMAX][AW]
+    static constexpr int TMASK = ANC + 4 * AW * NMAX;    // uint32[NMAX / 16]: tile (I, J) holds pairs
+    static constexpr int MISC = TMASK + 4 * (NMAX / 16); // int[16]
+    static constexpr int TOTAL = MISC + 64;
+};
+
+// One workgroup per (sequence, key head), 2 NMAX threads: the structure and
+// the Gram of the key head once, then the value heads of the key head two at
+// a time, thread t taking node t mod NMAX of head slot t / NMAX.
+template <int NMAX, int DK>
+__global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w) {
+    using L = TreeLds<NMAX, DK>;
+    constexpr int NTH = 2 * NMAX;
+    constexpr int NW = NTH / 64;
+    constexpr int KS = DK / 32;
+    constexpr int NTMAX = NMAX / 16;
+    constexpr int ZR = L::ZR;
+    constexpr int KCH = NMAX * DK / 8 / NTH;   // 16-byte pieces of K per thread
+    static_assert(KCH * NTH == NMAX * DK / 8, "K staging split");
+    constexpr int RU = NTMAX / NW;             // Gram row tiles per wavefront
+    static_assert(RU == 2, "row tiles w and 2 NW - 1 - w");
+
+    __shared__ __align__(16) unsigned char smem[L::TOTAL];
+    GDN_SPLIT_PHASE_DECL
+    GDN_SPLIT_PHASE(0);
+
+    const int N = a.N, Hk = a.H_k, Hv = a.H_v;
+    const int R = Hv / Hk;
+    const int b = blockIdx.x / Hk, kh = blockIdx.x % Hk;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ni = tid % NMAX, hr = tid / NMAX;
+
+    const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
+    const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
+
+    unsigned char* Ks = smem + L::KS;
+    float* xcb = reinterpret_cast<float*>(smem + L::KS);
+    float* kk = reinterpret_cast<float*>(smem + L::KK);
+    float* qk = reinterpret_cast<float*>(smem + L::QK);
+    uint8_t* pathc = smem + L::PATH;
+    uint8_t* pnode = smem + L::PNODE;
+    int* par = reinterpret_cast<int*>(smem + L::PAR);
+    int* dep = reinterpret_cast<int*>(smem + L::DEP);
+    int* nxt = reinterpret_cast<int*>(smem + L::NXT);
+    int* off = reinterpret_cast<int*>(smem + L::OFF);
+    float* gv = reinterpret_cast<float*>(smem + L::GV);
+    float* bet = reinterpret_cast<float*>(smem + L::BET);
+    float* Gs = reinterpret_cast<float*>(smem + L::GG);
+    uint32_t* anc = reinterpret_cast<uint32_t*>(smem + L::ANC);
+    uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + L::TMASK);
+    int* misc = reinterpret_cast<int*>(smem + L::MISC);
+
+    // ---- (1) Q rows of this wavefront's Gram row tiles (held in registers
+    // through the structure phases), parents, g and beta of the first two
+    // value heads, K
+    auto row_tile = [&](int u) { return u == 0 ? wave : 2 * NW - 1 - wave; };
+    bf16x8 qa[RU][KS];
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qa[u][ks] = load_frag(qg + ((static_cast<size_t>(b) * N + min(16 * row_tile(u) + lc, N - 1)) * Hk + kh) * DK +
+                                  8 * KS * lg + 8 * ks);
+    int p = -1;
+    if (tid < NMAX && tid < N) p = a.parent[static_cast<size_t>(b) * N + tid];
+    auto load_gb = [&](int r0) {
+        const int r = r0 + hr;
+        float gi = 0.f, bi = 0.f;
+        if (r < R && ni < N) {
+            const size_t nh = (static_cast<size_t>(b) * N + ni) * Hv + kh * R + r;
+            gi = a.g[nh];
+            bi = a.beta[nh];
+        }
+        gv[hr * NMAX + ni] = gi;
+        bet[hr * NMAX + ni] = bi;
+    };
+    load_gb(0);
+    {
+        uint4 kv[KCH];
+#pragma unroll
+        for (int q = 0; q < KCH; ++q) {
+            const int e = tid + q * NTH;
+            const int row = min(e / (DK / 8), N - 1);
+            kv[q] = *reinterpret_cast<const uint4*>(kg + ((static_cast<size_t>(b) * N + row) * Hk + kh) * DK + (e % (DK / 8)) * 8);
+        }
+#pragma unroll
+        for (int q = 0; q < KCH; ++q) {
+            const int e = tid + q * NTH;
+            const int row = e / (DK / 8), cc = e % (DK / 8);
+            const uint4 v = row < N ? kv[q] : make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint4*>(Ks + row * L::KROW + cc * 16) = v;
+        }
+    }
+    int bad_local = 0;
+    if (tid < NMAX) {
+        const int i = tid;
+        if (i < N && (p < -1 || p >= i)) {
+            bad_local = 1;
+            p = -1;
+        }
+        par[i] = p;
+        nxt[i] = p;
+        dep[i] = i < N ? 1 : 0;
+    }
+    if (tid < NTMAX) tmask[tid] = 0u;
+    const int bad = __syncthreads_or(bad_local);
+    GDN_SPLIT_PHASE(1);
+
+    // ---- (2) structure: depth by pointer jumping (dep[i] counts the nodes
+    // from i up to nxt[i]), pair offsets, root paths, ancestor bits
+    for (int round = 0; round < 9; ++round) {
+        int c2 = 0, n2 = -1;
+        if (tid < NMAX) {
+            const int nx = nxt[tid];
+            c2 = dep[tid] + (nx >= 0 ? dep[nx] : 0);
+            n2 = nx >= 0 ? nxt[nx] : -1;
+        }
+        __syncthreads();
+        if (tid < NMAX) {
+            dep[tid] = c2;
+            nxt[tid] = n2;
+        }
+        if (!__syncthreads_or(n2 >= 0)) break;
+    }
+    const int deep = __syncthreads_or(tid < N && dep[tid] > ZR);
+    GDN_SPLIT_PHASE(2);
+    if (kh == 0 && tid == 0) {
+        a.tree_status[b] = bad ? GDN_ERR_TREE : 0;
+        w.deep[b] = deep ? 1 : 0;
+    }
+    if (deep) return;
+    if (wave == 0) {
+        // exclusive scan of dep into off; off[N] = pair count
+        constexpr int E = NMAX / 64;
+        int vals[E];
+        int sum = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            vals[e] = dep[lane * E + e];
+            sum += vals[e];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+        }
+        int run = incl - sum;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            off[lane * E + e] = run;
+            run += vals[e];
+        }
+        if (lane == 63) {
+            off[NMAX] = incl;
+            misc[0] = incl;
+        }
+    }
+    __syncthreads();
+    const int total = misc[0];
+    if (tid < NMAX) {
+        const int i = tid;
+        uint32_t bits[L::AW];
+#pragma unroll
+        for (int q = 0; q < L::AW; ++q) bits[q] = 0u;
+        if (i < N) {
+            int pos = off[i] + dep[i] - 1;
+            uint32_t mask = 0u;
+            for (int s = i; s >= 0; s = par[s]) {
+                pathc[pos] = static_cast<uint8_t>(s);
+                pnode[pos] = static_cast<uint8_t>(i);
+                --pos;
+                mask |= 1u << (s >> 4);
+#pragma unroll
+                for (int q = 0; q < L::AW; ++q) bits[q] |= (s >> 5) == q ? 1u << (s & 31) : 0u;
+            }
+            atomicOr(&tmask[i >> 4], mask);
+        }
+#pragma unroll
+        for (int q = 0; q < L::AW; ++q) anc[i * L::AW + q] = bits[q];
+    }
+    __syncthreads();
+    GDN_SPLIT_PHASE(3);
+    if (kh == 0) {
+        // the sequence's pair structure for the dense kernel
+        int32_t* offg = w.off + static_cast<size_t>(b) * (N + 1);
+        for (int i = tid; i <= N; i += NTH) offg[i] = i < N ? off[i] : total;
+        uint8_t* pg = w.path + static_cast<size_t>(b) * w.P;
+        uint8_t* ng = w.pnode + static_cast<size_t>(b) * w.P;
+        for (int e = tid; e < total; e += NTH) {
+            pg[e] = pathc[e];
+            ng[e] = pnode[e];
+        }
+    }
+
+    // ---- (3) Gram values of the ancestor pairs: MFMA over the lower 16x16
+    // tiles that hold pairs; wavefront w takes row tiles w and 2 NW - 1 - w
+    // (their Q rows were loaded on entry)
+    {
+        const int NT = (N + 15) >> 4;
+        auto k_frag = [&](int row, int ks) -> bf16x8 {
+            return load_frag(Ks + row * L::KROW + 2 * (8 * KS * lg + 8 * ks));
+        };
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            const int I = row_tile(u);
+            if (I >= NT) continue;
+            const uint32_t tm = tmask[I];
+            bf16x8 ka[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) ka[ks] = k_frag(16 * I + lc, ks);
+            for (int J = 0; J <= I; ++J) {
+                if (!((tm >> J) & 1u)) continue;
+                f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 kb = k_frag(16 * J + lc, ks);
+                    akk = mfma(ka[ks], kb, akk);
+                    aqk = mfma(qa[u][ks], kb, aqk);
+                }
+                // lane: rows i = 16 I + 4 lg + rr, column node s = 16 J + lc;
+                // pair (i, s) sits at position dep[s] - 1 of i's root path
+                const int s = 16 * J + lc;
+                const int ds = dep[s];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int i = 16 * I + 4 * lg + rr;
+                    const uint32_t aw = anc[i * L::AW + (s >> 5)];
+                    if (i < N && ((aw >> (s & 31)) & 1u)) {
+                        const int pp = off[i] + ds - 1;
+                        kk[pp] = akk[rr];
+                        qk[pp] = aqk[rr];
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();   // K is no longer read: its area holds X from here on
+    GDN_SPLIT_PHASE(4);
+
+    // ---- (4) per pair of value heads: G, gamma; X; rows of Z~
+    float* xh = xcb + hr * L::XH;
+    for (int r0 = 0; r0 < R; r0 += 2) {
+        if (r0 > 0) {
+            __syncthreads();   // the previous pair's reads of gv, bet, Gs and X are done
+            load_gb(r0);
+            __syncthreads();
+        }
+        const int r = r0 + hr;
+        const bool live = r < R && ni < N;
+        const int h = kh * R + r;
+        const int o = off[ni], m = live ? dep[ni] : 0;
+        const float* gvh = gv + hr * NMAX;
+        float* Gh = Gs + hr * NMAX;
+        int t[ZR];
+#pragma unroll
+        for (int d = 0; d < ZR; ++d) t[d] = min(static_cast<int>(pathc[min(o + min(d, max(m - 1, 0)), L::CAP - 1)]), NMAX - 1);
+        float G = 0.f;
+#pragma unroll
+        for (int d = 0; d < ZR; ++d) G += d < m ? gvh[t[d]] : 0.f;
+        Gh[ni] = G;
+        if (live) w.gam[(static_cast<size_t>(b) * Hv + h) * N + ni] = __expf(G);
+        __syncthreads();
+        GDN_SPLIT_PHASE(5);
+        // X row of node ni (root first; the last entry, i itself, is not used)
+        const float bi = bet[hr * NMAX + ni];
+#pragma unroll
+        for (int d = 0; d < ZR; ++d)
+            if (d < m) xh[o + d] = bi * __expf(G - Gh[t[d]]) * kk[o + d];
+        if (ni < 32) xh[total + ni] = 0.f;   // pads read by the branch-free solve
+        __syncthreads();
+        GDN_SPLIT_PHASE(6);
+        if (live) {
+            // z (I + X) = y along the root path t_0 (root) .. t_{m-1} = i,
+            // swept from the node end: once z_a is final, z_b -= z_a X_{t_a, t_b}
+            // for b < a, X_{t_a, t_b} at position b of t_a's row.  Entries
+            // past the path are zero and their X reads land on finite values.
+            int oa[ZR];
+            float z[ZR];
+#pragma unroll
+            for (int d = 0; d < ZR; ++d) {
+                oa[d] = off[t[d]];
+                z[d] = d < m ? __expf(G - Gh[t[d]]) * qk[o + d] : 0.f;
+            }
+            float xr[ZR - 1];
+#pragma unroll
+            for (int e = 0; e < ZR - 1; ++e) xr[e] = xh[oa[ZR - 1] + e];
+#pragma unroll
+            for (int aa = ZR - 1; aa >= 1; --aa) {
+                float xn[ZR - 1];
+#pragma unroll
+                for (int e = 0; e + 1 < aa; ++e) xn[e] = xh[oa[aa - 1] + e];
+                const float za = z[aa];
+#pragma unroll
+                for (int e = 0; e < aa; ++e) z[e] -= za * xr[e];
+#pragma unroll
+                for (int e = 0; e + 1 < aa; ++e) xr[e] = xn[e];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float* zg = w.z + (static_cast<size_t>(b) * Hv + h) * w.P + o;
+#pragma unroll
+            for (int d = 0; d < ZR; ++d)
+                if (d < m) zg[d] = z[d] * bet[hr * NMAX + t[d]];
+        }
+    }
+    GDN_SPLIT_PHASE(7);
+    GDN_SPLIT_PHASE_END(0, blockIdx.x);
+}
+
+// --------------------------------------------------------------- dense kernel
+
+template <int NMAX, int DK, int DV>
+struct DenseLds {
+    static_assert(NMAX == 256, "trees of 129 to 256 nodes");
+    static constexpr int NTMAX = NMAX / 16;
+    static constexpr int CAP = NMAX * sp_zr(NMAX);
+    // K for K S0^T, in the k-slot order with chunks swizzled by row; once R'
+    // is formed, the same bytes hold three stages of one output row tile's
+    // Z~ blocks (bf16 hi + lo) and Q rows, tile I in stage I mod 3
+    static constexpr int KQ = 0;
+    static constexpr int ZT_BYTES = 2048 * (NTMAX / 2);          // NTMAX / 2 blocks of 2 KB
+    static constexpr int ZT = 0;                                  // [3][ZT_BYTES]
+    static constexpr int QT = ZT + 3 * ZT_BYTES;                  // [3] bf16[16][DK]
+    static constexpr int KQ_BYTES = sp_max(NMAX * DK * 2, QT + 3 * 32 * DK);
+    static constexpr int PATH = KQ + KQ_BYTES;                    // uint8[CAP]: ancestor of each pair
+    static constexpr int PNODE = PATH + CAP;                      // uint8[CAP]: node of each pair
+    static constexpr int GAM = PNODE + CAP;                       // float[NMAX]
+    static constexpr int OFF = GAM + 4 * NMAX;                    // int[NMAX + 16]: first pair of each node
+    static constexpr int MISC = OFF + 4 * (NMAX + 16);
+    // the per-node walk of a deep tree (S0 read from global memory): u
+    // [NMAX][64], G, k and q rows, parents
+    static constexpr int FB_G = NMAX * 64 * 4;
+    static constexpr int FB_KQ = FB_G + 4 * NMAX;
+    static constexpr int FB_PAR = FB_KQ + 8 * DK;
+    static constexpr int FB_END = FB_PAR + 4 * NMAX;
+    static constexpr int TOTAL = sp_max(MISC + 64, FB_END);
+    static_assert(DV != 128 || TOTAL <= 80 * 1024, "two workgroups per compute unit");
+};
+
+// One (sequence, value head) item per workgroup, d_v / 16 wavefronts, each
+// owning 16 value columns.
+template <int NMAX, int DK, int DV>
+__global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs a, SplitWs w) {
+    using L = DenseLds<NMAX, DK, DV>;
+    constexpr int NW = DV / 16;
+    constexpr int NTH = 64 * NW;
+    constexpr int KS = DK / 32;
+    constexpr int CH = DK / 8;             // 16-byte chunks per K/Q row
+    constexpr int NTMAX = NMAX / 16;
+    constexpr int NKMAX = NMAX / 32;
+
+    __shared__ __align__(16) unsigned char smem[L::TOTAL];
+    GDN_SPLIT_PHASE_DECL
+    GDN_SPLIT_PHASE(0);
+
+    const int N = a.N, Hk = a.H_k, Hv = a.H_v;
+    const int R = Hv / Hk;
+    const int n_items = a.B * Hv;
+    // Workgroups go to the 8 XCDs in turn; numbering the items so that each
+    // XCD takes a contiguous run keeps the value heads of one key head (which
+    // read the same K and Q) on one L2, dispatched close together
+    const int g = gridDim.x;
+    const int item = (g % 8 == 0 && g == n_items) ? (blockIdx.x % 8) * (g / 8) + blockIdx.x / 8 : blockIdx.x;
+    if (item >= n_items) return;
+    const int b = item / Hv, h = item % Hv, kh = h / R;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
+    const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
+    const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(a.v);
+    unsigned char* KQb = smem + L::KQ;
+    float* gam = reinterpret_cast<float*>(smem + L::GAM);
+    int* offs = reinterpret_cast<int*>(smem + L::OFF);
+
+    if (w.deep[b]) {
+        // a root path longer than the tree kernel solves: the per-node walk,
+        // by wavefront 0, one 64-column slice at a time
+        if (wave == 0) {
+            int* par_s = reinterpret_cast<int*>(smem + L::FB_PAR);
+            float* G_s = reinterpret_cast<float*>(smem + L::FB_G);
+            for (int i = lane; i < N; i += 64) {
+                const int pp = a.parent[static_cast<size_t>(b) * N + i];
+                par_s[i] = (pp < -1 || pp >= i) ? -1 : pp;
+            }
+            WaveSync::sync();
+            float* u_s = reinterpret_cast<float*>(smem);
+            float* ki = reinterpret_cast<float*>(smem + L::FB_KQ);
+            for (int c0 = 0; c0 < DV; c0 += 64)
+                walk_verify_slice_lds<uint16_t, DK, WaveSync>(a, b, h, c0, par_s, u_s, G_s, ki, ki + DK, nullptr);
+        }
+        return;
+    }
+
+    // ---- (1) loads: S0 rows and V of this wavefront's 16 value columns,
+    // the sequence's pair structure, gamma, K into LDS
+    // s0r[2 ks + hh]: d_k columns 32 ks + 16 hh + 4 lg .. + 3 of row col0 + lc;
+    // vr[S]: value columns col0 + 4 lg .. + 3 of node 16 S + lc
+    const int col0 = NW == 8 ? 32 * (wave & 3) + 16 * (wave >> 2) : 16 * wave;
+    float4 s0r[2 * KS];
+    {
+        const float4* src = reinterpret_cast<const float4*>(a.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + col0 + lc) * DK + 4 * lg);
+#pragma unroll
+        for (int q = 0; q < 2 * KS; ++q) s0r[q] = src[4 * q];
+    }
+    uint2 vr[NTMAX];
+    {
+        const uint16_t* vsrc = vg + static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV + col0 + 4 * lg;
+#pragma unroll
+        for (int S = 0; S < NTMAX; ++S)
+            vr[S] = *reinterpret_cast<const uint2*>(vsrc + static_cast<size_t>(min(16 * S + lc, N - 1)) * Hv * DV);
+    }
+    const int total = w.off[static_cast<size_t>(b) * (N + 1) + N];
+    const float* zsrc = w.z + (static_cast<size_t>(b) * Hv + h) * w.P;
+    {
+        // the byte arrays as 4-byte words (the pair capacity is a multiple of 4)
+        const uint32_t* ps = reinterpret_cast<const uint32_t*>(w.path + static_cast<size_t>(b) * w.P);
+        const uint32_t* ns = reinterpret_cast<const uint32_t*>(w.pnode + static_cast<size_t>(b) * w.P);
+        const int words = (total + 3) >> 2;
+        for (int e = tid; e < words; e += NTH) {
+            reinterpret_cast<uint32_t*>(smem + L::PATH)[e] = ps[e];
+            reinterpret_cast<uint32_t*>(smem + L::PNODE)[e] = ns[e];
+        }
+        for (int i = tid; i <= NMAX; i += NTH) offs[i] = w.off[static_cast<size_t>(b) * (N + 1) + min(i, N)];
+    }
+    float gm = 0.f;
+    if (tid < NMAX && tid < N) gm = w.gam[(static_cast<size_t>(b) * Hv + h) * N + tid];
+
+    // Natural 16-byte chunk c of K or Q row `row` into a buffer in the
+    // k-slot order the fragments read: element 32 ks + 16 hh + 4 g + r at
+    // position 32 ks + 8 g + 4 hh + r; chunk 4 ks + g stored at chunk
+    // position (4 ks + g) ^ (row mod CH); `keep` zeroes rows past N
+    auto put_chunk = [&](unsigned char* base, int row, int c, uint4 v, uint32_t keep) {
+        const int sw = row & (CH - 1);
+        const int ks = c >> 2, m = c & 3, hh = m >> 1, g0 = (m & 1) << 1;
+        const int rbase = row * (DK * 2) + 8 * hh;
+        *reinterpret_cast<uint2*>(base + rbase + (((4 * ks + g0) ^ sw) << 4)) = make_uint2(v.x & keep, v.y & keep);
+        *reinterpret_cast<uint2*>(base + rbase + (((4 * ks + g0 + 1) ^ sw) << 4)) = make_uint2(v.z & keep, v.w & keep);
+    };
+    {
+        // K in passes of at most 4 chunks per thread, which bounds the
+        // registers the staging holds beside the S0 and V loads in flight
+        constexpr int KCH = NMAX * CH / NTH;
+        static_assert(KCH * NTH == NMAX * CH, "K staging split");
+        constexpr int KP = KCH < 4 ? KCH : 4;
+        static_assert(KCH % KP == 0, "staging passes");
+#pragma unroll
+        for (int q0 = 0; q0 < KCH; q0 += KP) {
+            uint4 v[KP];
+#pragma unroll
+            for (int q = 0; q < KP; ++q) {
+                const int e = tid + (q0 + q) * NTH;
+                v[q] = *reinterpret_cast<const uint4*>(kg + ((static_cast<size_t>(b) * N + min(e / CH, N - 1)) * Hk + kh) * DK + (e % CH) * 8);
+            }
+#pragma unroll
+            for (int q = 0; q < KP; ++q) {
+                const int e = tid + (q0 + q) * NTH;
+                put_chunk(KQb, e / CH, e % CH, v[q], e / CH < N ? 0xFFFFFFFFu : 0u);
+            }
+        }
+    }
+    if (tid < NMAX) gam[tid] = gm;
+
+    // ---- (2) R' = V - gamma o (K S0^T) on MFMA, S0 as bf16 hi + lo; R' kept
+    // as fragments (k = node) of the Z~ R' product
+    const int NT = (N + 15) >> 4;
+    s16x4 eye;   // identity for the V transposes: lane (n, g) holds B[4 g + j][n]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) eye[q] = 4 * lg + q == lc ? static_cast<short>(0x3F80) : short(0);
+    bf16x8 s0h[KS], s0l[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const float4 x0 = s0r[2 * ks], x1 = s0r[2 * ks + 1];
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        split8(x, s0h[ks], s0l[ks]);
+    }
+    __syncthreads();
+    GDN_SPLIT_PHASE(1);
+    bf16x8 rh[NKMAX], rl[NKMAX];
+#pragma unroll
+    for (int kap = 0; kap < NKMAX; ++kap) {
+        float rt[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int S = 2 * kap + half;
+            if (S < NT) {
+                f32x4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int row = 16 * S + lc;
+                    const bf16x8 fa = load_frag(KQb + row * (DK * 2) + (((4 * ks + lg) ^ (row & (CH - 1))) << 4));
+                    ah = mfma(fa, s0h[ks], ah);
+                    al = mfma(fa, s0l[ks], al);
+                }
+                const f32x4 gq = *reinterpret_cast<const f32x4*>(gam + 16 * S + 4 * lg);
+                const f32x4 vt = mfma16(__builtin_bit_cast(s16x4, vr[S]), eye, f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 pk = ah + al;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float vv = 16 * S + 4 * lg + rr < N ? vt[rr] : 0.f;
+                    rt[4 * half + rr] = vv - gq[rr] * pk[rr];
+                }
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) rt[4 * half + rr] = 0.f;
+            }
+        }
+        split8(rt, rh[kap], rl[kap]);
+    }
+    GDN_SPLIT_PHASE(2);
+
+    // ---- (3) O tiles, O^T = gamma o (S0 Q^T) + R'^T Z~^T, each with its Q
+    // rows and its blocks of Z~ staged in LDS by the workgroup, three stages
+    // deep so that one barrier per tile orders everything: in the step of
+    // tile I the workgroup fills stage I + 1 (zeroed one step earlier) with
+    // that tile's pairs (contiguous in pair order) and Q rows, contracts tile
+    // I, and zeroes stage I + 2 (last read by tile I - 1).  The pair values
+    // and Q rows come from global memory one step ahead of their stage.
+    // Block kap of a stage holds nodes 32 kap..; node t of row i sits in lane
+    // group ((t >> 2) & 3), slot 4 ((t >> 4) & 1) + (t & 3).
+    const uint8_t* pathc = smem + L::PATH;
+    const uint8_t* pnode = smem + L::PNODE;
+    auto zt = [&](int I) { return smem + L::ZT + L::ZT_BYTES * (I % 3); };
+    auto qt = [&](int I) { return smem + L::QT + 32 * DK * (I % 3); };
+    static_assert(16 * CH <= NTH, "one Q piece per thread");
+    constexpr int TP = (16 * sp_zr(NMAX) + NTH - 1) / NTH;   // pairs of a tile per thread
+    // uniform bases with 32-bit lane offsets: no per-lane 64-bit addresses
+    // held across the loop
+    const uint16_t* qb = qg + (static_cast<size_t>(b) * N * Hk + kh) * DK;
+    float* ob = a.o + (static_cast<size_t>(b) * N * Hv + h) * DV;
+    auto load_q = [&](int I, int t) {
+        const uint32_t row = min(16 * I + t / CH, N - 1);
+        return *reinterpret_cast<const uint4*>(qb + row * static_cast<uint32_t>(Hk * DK) + 8u * (t % CH));
+    };
+    // the pairs of tile I that thread t scatters (p = -1: none)
+    auto load_z = [&](int I, int t, int (&p)[TP], float (&zz)[TP]) {
+        const int p0 = I < NT ? offs[16 * I] : total;
+        const int p1 = I < NT ? offs[min(16 * I + 16, N)] : total;
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            p[u] = p0 + t + u * NTH < p1 ? p0 + t + u * NTH : -1;
+            zz[u] = zsrc[static_cast<uint32_t>(p[u] >= 0 ? p[u] : 0)];
+        }
+    };
+    auto fill = [&](int I, int t, const uint4& qv, const int (&p)[TP], const float (&zz)[TP]) {
+        unsigned char* Zt = zt(I);
+        if (t < 16 * CH) put_chunk(qt(I), t / CH, t % CH, qv, 16 * I + t / CH < N ? 0xFFFFFFFFu : 0u);
+#pragma unroll
+        for (int u = 0; u < TP; ++u) {
+            if (p[u] >= 0) {
+                const int i = pnode[p[u]], tn = pathc[p[u]];
+                const __bf16 zh = static_cast<__bf16>(zz[u]);
+                const __bf16 zl = static_cast<__bf16>(zz[u] - static_cast<float>(zh));
+                const int el = (((((tn >> 2) & 3) << 4) | (i & 15)) << 3) + (((tn >> 4) & 1) << 2) + (tn & 3);
+                unsigned char* blk = Zt + 2048 * (tn >> 5);
+                reinterpret_cast<__bf16*>(blk)[el] = zh;
+                reinterpret_cast<__bf16*>(blk + 1024)[el] = zl;
+            }
+        }
+    };
+    auto zero = [&](int I) {
+        const int nb = I / 2 + 1;
+        for (int e = tid; e < nb * 128; e += NTH) reinterpret_cast<uint4*>(zt(I))[e] = make_uint4(0u, 0u, 0u, 0u);
+    };
+    // o is written once: plain stores, whose two 64-byte halves of each
+    // 128-byte row piece (from the two wavefronts of one SIMD) meet in L2
+    auto store_o = [&](int I, int ln, const f32x4& v) {
+        const int i = 16 * I + (ln & 15);
+        if (i < N)
+            *reinterpret_cast<f32x4*>(ob + (static_cast<uint32_t>(i) * static_cast<uint32_t>(Hv * DV) +
+                                            static_cast<uint32_t>(col0 + 4 * (ln >> 4)))) = v;
+    };
+
+    __syncthreads();   // K is no longer read
+    int pn[TP];
+    float zv[TP];
+    uint4 qv = load_q(0, tid);
+    load_z(0, tid, pn, zv);
+    zero(0);
+    if (NT > 1) zero(1);
+    __syncthreads();
+    fill(0, tid, qv, pn, zv);
+    qv = load_q(min(1, NT - 1), tid);
+    load_z(1, tid, pn, zv);
+    GDN_SPLIT_PHASE(3);
+    // The o stores of tile I - 1 are issued in the step of tile I, after its
+    // wait for the prefetched rows: loads and stores share one wait counter,
+    // so a wait for a load also waits for stores issued before it, and this
+    // keeps those stores a whole tile old.
+    f32x4 prev = {0.f, 0.f, 0.f, 0.f};
+    for (int I = 0; I < NT; ++I) {
+        // lane indices through an opaque copy: offsets derived from them are
+        // formed per tile instead of held in registers
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        const int ln = t & 63, c16 = ln & 15;
+        __syncthreads();
+        if (I + 1 < NT) fill(I + 1, t, qv, pn, zv);
+        if (I > 0) store_o(I - 1, ln, prev);
+        if (I + 1 < NT) {
+            qv = load_q(min(I + 2, NT - 1), t);
+            load_z(I + 2, t, pn, zv);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const unsigned char* Qt = qt(I);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 fb = load_frag(Qt + c16 * (DK * 2) + (((4 * ks + (ln >> 4)) ^ (c16 & (CH - 1))) << 4));
+            acc = mfma(s0h[ks], fb, acc);
+            acc = mfma(s0l[ks], fb, acc);
+        }
+        acc *= gam[16 * I + c16];
+        const unsigned char* blk = zt(I) + 16 * ln;
+        const int nb = I / 2 + 1;
+#pragma unroll
+        for (int kap = 0; kap < NKMAX; ++kap) {
+            if (kap < nb) {
+                const bf16x8 zh = load_frag(blk + 2048 * kap);
+                const bf16x8 zl = load_frag(blk + 2048 * kap + 1024);
+                acc = mfma(rh[kap], zh, acc);
+                acc = mfma(rl[kap], zh, acc);
+                acc = mfma(rh[kap], zl, acc);
+            }
+        }
+        prev = acc;
+        if (I + 2 < NT) zero(I + 2);
+    }
+    store_o(NT - 1, lane, prev);
+    GDN_SPLIT_PHASE(4);
+    GDN_SPLIT_PHASE_END(1, item);
+}
+
+template <int NMAX, int DK, int DV>
+hipError_t launch_split_t(const VerifyArgs& a, const SplitWs& w, hipStream_t stream) {
+    hipLaunchKernelGGL((tree_kernel<NMAX, DK>), dim3(static_cast<unsigned>(a.B) * a.H_k), dim3(2 * NMAX), 0, stream, a, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dense_kernel<NMAX, DK, DV>), dim3(static_cast<unsigned>(a.B) * a.H_v), dim3(4 * DV), 0, stream, a, w);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_verify_split(const VerifyArgs& a, hipStream_t stream) {
+    if (!a.split_ws || a.N <= 128 || a.N > 256) return hipErrorInvalidValue;
+    const SplitWs w = split_ws_at(a.split_ws, a.B, a.N, a.H_v);
+    if (a.d_k == 128)
+        return a.d_v == 128 ? launch_split_t<256, 128, 128>(a, w, stream) : launch_split_t<256, 128, 64>(a, w, stream);
+    return a.d_v == 128 ? launch_split_t<256, 64, 128>(a, w, stream) : launch_split_t<256, 64, 64>(a, w, stream);
+}
+
+}  // namespace gdn

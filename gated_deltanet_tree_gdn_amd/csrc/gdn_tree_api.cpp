@@ -21,6 +21,7 @@
 struct gdn_ctx {
     gdn_tree_dims dims;
     int32_t* status;  // device: [B] tree verdicts, then [B] accept verdicts
+    void* split;      // device: the two-launch verify's workspace (after the verdicts)
     bool validate;    // GDN_VALIDATE=1: synchronous host checks of parent/accepted
     bool force_walk;  // GDN_FORCE_SIMPLE=1: per-node walk kernels only
     bool have_verify;
@@ -120,9 +121,15 @@ void set_last_error(const std::string& msg) { g_last_error = msg; }
 
 extern "C" {
 
+namespace {
+size_t status_bytes(const gdn_tree_dims* dims) {
+    return round256(2 * static_cast<size_t>(dims->B > 0 ? dims->B : 1) * sizeof(int32_t));
+}
+}  // namespace
+
 size_t gdn_tree_workspace_bytes(const gdn_tree_dims* dims) {
     if (!dims || dims->B < 0) return 0;
-    return round256(2 * static_cast<size_t>(dims->B > 0 ? dims->B : 1) * sizeof(int32_t));
+    return status_bytes(dims) + gdn::split_ws_bytes(dims->B, dims->N, dims->H_v);
 }
 
 gdn_status gdn_ctx_create(const gdn_tree_dims* dims, void* workspace, size_t workspace_bytes,
@@ -139,6 +146,9 @@ gdn_status gdn_ctx_create(const gdn_tree_dims* dims, void* workspace, size_t wor
     if (!c) return fail(GDN_ERR_WORKSPACE, "out of host memory");
     c->dims = *dims;
     c->status = static_cast<int32_t*>(workspace);
+    c->split = gdn::split_ws_bytes(dims->B, dims->N, dims->H_v) > 0
+                   ? static_cast<unsigned char*>(workspace) + status_bytes(dims)
+                   : nullptr;
     const char* env = std::getenv("GDN_VALIDATE");
     c->validate = env && std::strcmp(env, "1") == 0;
     const char* fw = std::getenv("GDN_FORCE_SIMPLE");
@@ -178,7 +188,7 @@ gdn_status verify_with(hipError_t (*launch)(const gdn::VerifyArgs&, hipStream_t)
     GDN_TRY(check_ptr(o, "o"));
     if (ctx->validate) GDN_TRY(host_check_tree(d, parent, stream));
     gdn::VerifyArgs a{d.B, d.N, d.H_k, d.H_v, d.d_k, d.d_v, d.qkv_dtype, q, k, v, g, beta, parent, S0, o,
-                      ctx->status, ctx->force_walk ? 1 : 0};
+                      ctx->status, ctx->force_walk ? 1 : 0, ctx->split};
     hipError_t e = launch(a, stream);
     if (e != hipSuccess) return hip_fail(e, what);
     ctx->have_verify = true;
@@ -260,7 +270,7 @@ gdn_status gdn_commit_verify(gdn_ctx* ctx, const int32_t* accepted, const void* 
         e = gdn::launch_commit(ca, stream);
     } else {
         gdn::VerifyArgs va{d.B, d.N, d.H_k, d.H_v, d.d_k, d.d_v, d.qkv_dtype, q, k, v, g, beta, parent, S_next, o,
-                           ctx->status, ctx->force_walk ? 1 : 0};
+                           ctx->status, ctx->force_walk ? 1 : 0, ctx->split};
         if (d.qkv_dtype == GDN_BF16 && d.N <= 128 && !ctx->force_walk) {
             gdn::CommitPrev cp{ctx->k, ctx->v, ctx->g, ctx->beta, ctx->parent, ctx->S0, accepted, S_next,
                                ctx->status + d.B};

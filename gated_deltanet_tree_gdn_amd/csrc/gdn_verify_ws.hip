@@ -172,7 +172,6 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
     constexpr int CH = DK / 8;           // 16-byte chunks per K/Q row
     constexpr int NTMAX = NMAX / 16;
     constexpr int NKMAX = NMAX / 32;
-    constexpr int KCH = (NMAX * CH + TTH - 1) / TTH;  // K/Q chunks staged per tree thread
     constexpr int ZR = 16;
     static_assert(NMAX <= TTH, "one node per tree thread");
     static_assert(CT >= 1 && CW * NWD == DV, "whole 16-column tiles per dense wavefront");

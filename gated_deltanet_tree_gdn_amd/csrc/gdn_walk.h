@@ -124,7 +124,9 @@ __device__ void walk_verify_slice(const VerifyArgs& a, int b, int h, int c0, con
 
 // The same walk with the slice's S0 rows staged in LDS (s0_s: [DK][64],
 // column-major so lane c reads consecutive words) instead of registers, for
-// use inside kernels whose register budget is set by other work.
+// use inside kernels whose register budget is set by other work; with
+// s0_s == nullptr each lane reads its S0 row from global memory instead
+// (for kernels whose LDS budget is set by other work).
 template <typename T, int DK, class Sync>
 __device__ void walk_verify_slice_lds(const VerifyArgs& a, int b, int h, int c0, const int* par_s, float* u_s,
                                       float* G_s, float* ki_s, float* qi_s, float* s0_s) {
@@ -137,8 +139,14 @@ __device__ void walk_verify_slice_lds(const VerifyArgs& a, int b, int h, int c0,
     const T* __restrict__ v = static_cast<const T*>(a.v);
 
     const float* S0row = a.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + c) * DK;
-    for (int j = 0; j < DK; ++j) s0_s[j * 64 + lane] = S0row[j];
-    Sync::sync();
+    const float* s0p = S0row;
+    int s0_step = 1;
+    if (s0_s) {
+        for (int j = 0; j < DK; ++j) s0_s[j * 64 + lane] = S0row[j];
+        Sync::sync();
+        s0p = s0_s + lane;
+        s0_step = 64;
+    }
 
     for (int i = 0; i < N; ++i) {
         const int p = par_s[i];
@@ -155,7 +163,7 @@ __device__ void walk_verify_slice_lds(const VerifyArgs& a, int b, int h, int c0,
 
         float sk = 0.f, sq = 0.f;
         for (int j = 0; j < DK; ++j) {
-            const float sv = s0_s[j * 64 + lane];
+            const float sv = s0p[j * s0_step];
             sk += sv * ki_s[j];
             sq += sv * qi_s[j];
         }

@@ -1,9 +1,12 @@
 """The allocation-free verify (gdn_tree_verify_static, for callers that
 cannot allocate device memory) against the context entry point
 (gdn_tree_verify) through the C ABI: two calls in a row on one GPU, the
-second on a smaller input, each bit-identical to gdn_tree_verify on the same
-input (both run the same kernels) and, on the smaller cases, within the
-oracle bars (rel-L2 <= 1e-3, max-abs <= 5e-3) of the fp64 oracle."""
+second on a smaller input.  Where both run the same kernels (trees of at
+most 128 nodes, and fp32 q/k/v) the outputs are bit-identical; for larger
+bf16 trees the context runs the two-launch verify over its workspace and
+the static entry point the single-launch kernel, so there they agree within
+the oracle bars (rel-L2 <= 1e-3, max-abs <= 5e-3).  On the smaller cases both
+are also checked against the fp64 oracle at those bars."""
 import sys
 
 import numpy as np
@@ -48,7 +51,15 @@ def static_then_context(cfg, inp, d, check_oracle):
     gdn.gdn_ctx_status(ctx)
     got = o.cpu().numpy()
     assert np.isfinite(got).all()
-    assert np.array_equal(got.view(np.uint32), want.cpu().numpy().view(np.uint32))
+    ref_ctx = want.cpu().numpy()
+    if cfg.N <= 128 or cfg.dtype != "bf16":
+        assert np.array_equal(got.view(np.uint32), ref_ctx.view(np.uint32))
+    else:
+        x, y = got.astype(np.float64), ref_ctx.astype(np.float64)
+        rel = np.linalg.norm(x - y) / np.linalg.norm(y)
+        mab = float(np.abs(x - y).max())
+        say(f"  against the context path: rel-L2 {rel:.3e} max-abs {mab:.3e}")
+        assert rel <= 1e-3 and mab <= 5e-3
     if check_oracle:
         ref = oracle.verify_inputs(inp)
         x = got.astype(np.float64)
