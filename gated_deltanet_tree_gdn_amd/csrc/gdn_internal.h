@@ -38,8 +38,7 @@ struct VerifyArgs {
 struct SplitWs {
     float* z;        // [B][H_v][P]
     float* gam;      // [B][H_v][N]
-    uint8_t* path;   // [B][P]: ancestor of each pair
-    uint8_t* pnode;  // [B][P]: node of each pair
+    uint16_t* zoff;  // [B][P]: byte offset of each pair's Z~ entry in its output tile's blocks
     int32_t* off;    // [B][N + 1]: first pair of each node, then the count
     int32_t* deep;   // [B]: 1 for a root path the tree kernel does not solve
     int P;           // pair capacity per sequence
@@ -47,7 +46,7 @@ struct SplitWs {
 // Byte offsets of the arrays in the workspace (each 256-aligned); pairs per
 // sequence at most N ZR, ZR the longest root path the tree kernel solves.
 struct SplitLayout {
-    size_t z, gam, path, pnode, off, deep, total;
+    size_t z, gam, zoff, off, deep, total;
     int P;
 };
 inline int split_zr(int N) { return N > 128 ? 24 : 16; }
@@ -58,9 +57,8 @@ inline SplitLayout split_layout(int B, int N, int Hv) {
     const size_t b = B > 0 ? B : 1, n = N > 0 ? N : 1, h = Hv > 0 ? Hv : 1;
     l.z = 0;
     l.gam = l.z + r256(b * h * l.P * sizeof(float));
-    l.path = l.gam + r256(b * h * n * sizeof(float));
-    l.pnode = l.path + r256(b * l.P);
-    l.off = l.pnode + r256(b * l.P);
+    l.zoff = l.gam + r256(b * h * n * sizeof(float));
+    l.off = l.zoff + r256(b * l.P * sizeof(uint16_t));
     l.deep = l.off + r256(b * (n + 1) * sizeof(int32_t));
     l.total = l.deep + r256(b * sizeof(int32_t));
     return l;
@@ -73,8 +71,7 @@ inline SplitWs split_ws_at(void* base, int B, int N, int Hv) {
     SplitWs w;
     w.z = reinterpret_cast<float*>(p + l.z);
     w.gam = reinterpret_cast<float*>(p + l.gam);
-    w.path = p + l.path;
-    w.pnode = p + l.pnode;
+    w.zoff = reinterpret_cast<uint16_t*>(p + l.zoff);
     w.off = reinterpret_cast<int32_t*>(p + l.off);
     w.deep = reinterpret_cast<int32_t*>(p + l.deep);
     w.P = l.P;

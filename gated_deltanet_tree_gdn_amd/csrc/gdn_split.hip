@@ -36,8 +36,8 @@
 //   z     float [B][H_v][P]  Z~ values in pair order (below), times beta of
 //                            the ancestor
 //   gam   float [B][H_v][N]  gamma
-//   path  uint8 [B][P]       the ancestor s of each pair
-//   pnode uint8 [B][P]       the node i of each pair
+//   zoff  uint16 [B][P]      where each pair's entry goes in the MFMA blocks
+//                            of its output row tile (below)
 //   off   int32 [B][N + 1]   first pair of each node; off[N] = pair count
 //   deep  int32 [B]          1: a root path longer than ZR nodes (the
 //                            dense kernel walks that sequence per node)
@@ -75,16 +75,14 @@ template <int NMAX, int DK>
 struct TreeLds {
     static constexpr int ZR = sp_zr(NMAX);
     static constexpr int CAP = NMAX * ZR;
-    static constexpr int AW = NMAX / 32;                 // ancestor bit-row words
     static constexpr int KROW = DK * 2 + 16;             // staged k row, padded against bank conflicts
     static constexpr int KS_BYTES = NMAX * KROW;
     static constexpr int XH = CAP + 32;                  // X of one value head (32 zero pads)
     static constexpr int KS = 0;                         // K rows; after the Gram, X of two value heads
     static constexpr int KK = sp_align(sp_max(KS_BYTES, 2 * 4 * XH), 16);  // float[CAP + 4]: k_i . k_s
     static constexpr int QK = KK + 4 * (CAP + 4);        // float[CAP + 4]: q_i . k_s
-    static constexpr int PATH = QK + 4 * (CAP + 4);      // uint8[CAP]
-    static constexpr int PNODE = PATH + CAP;             // uint8[CAP]
-    static constexpr int NODE = sp_align(PNODE + CAP, 16);
+    static constexpr int PATH = QK + 4 * (CAP + 4);      // uint8[CAP]: ancestor of each pair
+    static constexpr int NODE = sp_align(PATH + CAP, 16);
     static constexpr int PAR = NODE;                     // int[NMAX]
     static constexpr int DEP = PAR + 4 * NMAX;           // int[NMAX]: nodes on the root path
     static constexpr int NXT = DEP + 4 * NMAX;           // int[NMAX]: pointer jumping
@@ -92,8 +90,7 @@ struct TreeLds {
     static constexpr int GV = OFF + 4 * (NMAX + 16);     // float[2][NMAX]: g of two value heads
     static constexpr int BET = GV + 8 * NMAX;            // float[2][NMAX]: beta
     static constexpr int GG = BET + 8 * NMAX;            // float[2][NMAX]: G
-    static constexpr int ANC = GG + 8 * NMAX;            // uint32[NMAX][AW]
-    static constexpr int TMASK = ANC + 4 * AW * NMAX;    // uint32[NMAX / 16]: tile (I, J) holds pairs
+    static constexpr int TMASK = GG + 8 * NMAX;          // uint32[NMAX / 16]: tile (I, J) holds pairs
     static constexpr int MISC = TMASK + 4 * (NMAX / 16); // int[16]
     static constexpr int TOTAL = MISC + 64;
 };
@@ -134,7 +131,6 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
     float* kk = reinterpret_cast<float*>(smem + L::KK);
     float* qk = reinterpret_cast<float*>(smem + L::QK);
     uint8_t* pathc = smem + L::PATH;
-    uint8_t* pnode = smem + L::PNODE;
     int* par = reinterpret_cast<int*>(smem + L::PAR);
     int* dep = reinterpret_cast<int*>(smem + L::DEP);
     int* nxt = reinterpret_cast<int*>(smem + L::NXT);
@@ -142,7 +138,6 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
     float* gv = reinterpret_cast<float*>(smem + L::GV);
     float* bet = reinterpret_cast<float*>(smem + L::BET);
     float* Gs = reinterpret_cast<float*>(smem + L::GG);
-    uint32_t* anc = reinterpret_cast<uint32_t*>(smem + L::ANC);
     uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + L::TMASK);
     int* misc = reinterpret_cast<int*>(smem + L::MISC);
 
@@ -254,39 +249,33 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
     }
     __syncthreads();
     const int total = misc[0];
-    if (tid < NMAX) {
+    if (tid < NMAX && tid < N) {
+        // node i's root path, root first, at its pairs; the tiles that hold
+        // pairs; (key head 0) where each pair's entry goes in the dense
+        // kernel's blocks: block s / 32 (2 KB: 1 KB hi, then 1 KB lo) of the
+        // row tile, lane group (s / 4) mod 4, row i mod 16, slot
+        // 4 ((s / 16) mod 2) + s mod 4 of that lane's 8 bf16
         const int i = tid;
-        uint32_t bits[L::AW];
-#pragma unroll
-        for (int q = 0; q < L::AW; ++q) bits[q] = 0u;
-        if (i < N) {
-            int pos = off[i] + dep[i] - 1;
-            uint32_t mask = 0u;
-            for (int s = i; s >= 0; s = par[s]) {
-                pathc[pos] = static_cast<uint8_t>(s);
-                pnode[pos] = static_cast<uint8_t>(i);
-                --pos;
-                mask |= 1u << (s >> 4);
-#pragma unroll
-                for (int q = 0; q < L::AW; ++q) bits[q] |= (s >> 5) == q ? 1u << (s & 31) : 0u;
+        uint16_t* zg = w.zoff + static_cast<size_t>(b) * w.P;
+        int pos = off[i] + dep[i] - 1;
+        uint32_t mask = 0u;
+        for (int s = i; s >= 0; s = par[s]) {
+            pathc[pos] = static_cast<uint8_t>(s);
+            if (kh == 0) {
+                const int el = (((((s >> 2) & 3) << 4) | (i & 15)) << 3) + (((s >> 4) & 1) << 2) + (s & 3);
+                zg[pos] = static_cast<uint16_t>(2048 * (s >> 5) + 2 * el);
             }
-            atomicOr(&tmask[i >> 4], mask);
+            --pos;
+            mask |= 1u << (s >> 4);
         }
-#pragma unroll
-        for (int q = 0; q < L::AW; ++q) anc[i * L::AW + q] = bits[q];
+        atomicOr(&tmask[i >> 4], mask);
     }
     __syncthreads();
     GDN_SPLIT_PHASE(3);
     if (kh == 0) {
-        // the sequence's pair structure for the dense kernel
+        // the rest of the sequence's pair structure for the dense kernel
         int32_t* offg = w.off + static_cast<size_t>(b) * (N + 1);
         for (int i = tid; i <= N; i += NTH) offg[i] = i < N ? off[i] : total;
-        uint8_t* pg = w.path + static_cast<size_t>(b) * w.P;
-        uint8_t* ng = w.pnode + static_cast<size_t>(b) * w.P;
-        for (int e = tid; e < total; e += NTH) {
-            pg[e] = pathc[e];
-            ng[e] = pnode[e];
-        }
     }
 
     // ---- (3) Gram values of the ancestor pairs: MFMA over the lower 16x16
@@ -305,29 +294,64 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
             bf16x8 ka[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) ka[ks] = k_frag(16 * I + lc, ks);
-            for (int J = 0; J <= I; ++J) {
-                if (!((tm >> J) & 1u)) continue;
+            // this lane's rows i = 16 I + 4 lg + rr: first pair and depth
+            int oi[4], di[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = 16 * I + 4 * lg + rr;
+                oi[rr] = off[i];
+                di[rr] = i < N ? dep[i] : 0;
+            }
+            // tiles J <= I that hold pairs, in order; the K fragments of tile
+            // J, the depth of its node s = 16 J + lc and the root-path bytes
+            // at which the lane's four pairs (i, s) would sit are read one
+            // tile ahead
+            const uint32_t todo = tm & ((2u << I) - 1u);
+            struct Ahead {
+                bf16x8 kb[KS];
+                int ds;
+                int pc[4];
+            };
+            auto read_ahead = [&](int J) __attribute__((always_inline)) {
+                Ahead r;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) r.kb[ks] = k_frag(16 * J + lc, ks);
+                r.ds = dep[16 * J + lc];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) r.pc[rr] = pathc[min(max(oi[rr] + r.ds - 1, 0), L::CAP - 1)];
+                return r;
+            };
+            uint32_t left = todo;
+            if (!left) continue;
+            int J = __builtin_ctz(left);
+            left &= left - 1;
+            Ahead cur = read_ahead(J);
+            for (;;) {
                 f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 kb = k_frag(16 * J + lc, ks);
-                    akk = mfma(ka[ks], kb, akk);
-                    aqk = mfma(qa[u][ks], kb, aqk);
+                    akk = mfma(ka[ks], cur.kb[ks], akk);
+                    aqk = mfma(qa[u][ks], cur.kb[ks], aqk);
                 }
+                const int Jn = left ? __builtin_ctz(left) : -1;
+                left &= left - 1;
+                Ahead nxt;
+                if (Jn >= 0) nxt = read_ahead(Jn);
                 // lane: rows i = 16 I + 4 lg + rr, column node s = 16 J + lc;
-                // pair (i, s) sits at position dep[s] - 1 of i's root path
-                const int s = 16 * J + lc;
-                const int ds = dep[s];
+                // s is an ancestor of i (or i) exactly when i's root path
+                // holds s at position dep[s] - 1, where the pair is stored
+                const int sn = 16 * J + lc;
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    const int i = 16 * I + 4 * lg + rr;
-                    const uint32_t aw = anc[i * L::AW + (s >> 5)];
-                    if (i < N && ((aw >> (s & 31)) & 1u)) {
-                        const int pp = off[i] + ds - 1;
+                    if (cur.ds >= 1 && cur.ds <= di[rr] && cur.pc[rr] == sn) {
+                        const int pp = oi[rr] + cur.ds - 1;
                         kk[pp] = akk[rr];
                         qk[pp] = aqk[rr];
                     }
                 }
+                if (Jn < 0) break;
+                J = Jn;
+                cur = nxt;
             }
         }
     }
@@ -418,9 +442,8 @@ struct DenseLds {
     static constexpr int ZT = 0;                                  // [3][ZT_BYTES]
     static constexpr int QT = ZT + 3 * ZT_BYTES;                  // [3] bf16[16][DK]
     static constexpr int KQ_BYTES = sp_max(NMAX * DK * 2, QT + 3 * 32 * DK);
-    static constexpr int PATH = KQ + KQ_BYTES;                    // uint8[CAP]: ancestor of each pair
-    static constexpr int PNODE = PATH + CAP;                      // uint8[CAP]: node of each pair
-    static constexpr int GAM = PNODE + CAP;                       // float[NMAX]
+    static constexpr int ZOFF = KQ + KQ_BYTES;                    // uint16[CAP]: each pair's place in its tile's blocks
+    static constexpr int GAM = ZOFF + 2 * CAP;                    // float[NMAX]
     static constexpr int OFF = GAM + 4 * NMAX;                    // int[NMAX + 16]: first pair of each node
     static constexpr int MISC = OFF + 4 * (NMAX + 16);
     // the per-node walk of a deep tree (S0 read from global memory): u
@@ -430,20 +453,23 @@ struct DenseLds {
     static constexpr int FB_PAR = FB_KQ + 8 * DK;
     static constexpr int FB_END = FB_PAR + 4 * NMAX;
     static constexpr int TOTAL = sp_max(MISC + 64, FB_END);
-    static_assert(DV != 128 || TOTAL <= 80 * 1024, "two workgroups per compute unit");
+    static_assert(TOTAL <= 80 * 1024, "two workgroups per compute unit");
 };
 
-// One (sequence, value head) item per workgroup, d_v / 16 wavefronts, each
-// owning 16 value columns.
-template <int NMAX, int DK, int DV>
-__global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs a, SplitWs w) {
+// One (sequence, value head) item per workgroup; each wavefront owns CT
+// tiles of 16 value columns (two at d_v = 128: every Z~ block and Q row read
+// from LDS then serves two column tiles, and a wavefront writes whole
+// 128-byte pieces of o rows).
+template <int NMAX, int DK, int DV, int CT>
+__global__ __launch_bounds__(4 * DV / CT, 2) void dense_kernel(VerifyArgs a, SplitWs w) {
     using L = DenseLds<NMAX, DK, DV>;
-    constexpr int NW = DV / 16;
+    constexpr int NW = DV / (16 * CT);
     constexpr int NTH = 64 * NW;
     constexpr int KS = DK / 32;
     constexpr int CH = DK / 8;             // 16-byte chunks per K/Q row
     constexpr int NTMAX = NMAX / 16;
     constexpr int NKMAX = NMAX / 32;
+    static_assert(NW * 16 * CT == DV, "whole column tiles per wavefront");
 
     __shared__ __align__(16) unsigned char smem[L::TOTAL];
     GDN_SPLIT_PHASE_DECL
@@ -489,39 +515,40 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
         return;
     }
 
-    // ---- (1) loads: S0 rows and V of this wavefront's 16 value columns,
-    // the sequence's pair structure, gamma, K into LDS
-    // s0r[2 ks + hh]: d_k columns 32 ks + 16 hh + 4 lg .. + 3 of row col0 + lc;
-    // vr[S]: value columns col0 + 4 lg .. + 3 of node 16 S + lc
-    const int col0 = NW == 8 ? 32 * (wave & 3) + 16 * (wave >> 2) : 16 * wave;
-    float4 s0r[2 * KS];
-    {
-        const float4* src = reinterpret_cast<const float4*>(a.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + col0 + lc) * DK + 4 * lg);
+    // ---- (1) loads: S0 rows and V of this wavefront's value columns, the
+    // sequence's pair structure, gamma, K into LDS.  Column tile st of the
+    // wavefront covers columns col0 + 16 st ..; s0r[st][2 ks + hh]: d_k
+    // columns 32 ks + 16 hh + 4 lg .. + 3 of row col0 + 16 st + lc; vr[st][S]:
+    // value columns col0 + 16 st + 4 lg .. + 3 of node 16 S + lc
+    const int col0 = 16 * CT * wave;
+    float4 s0r[CT][2 * KS];
 #pragma unroll
-        for (int q = 0; q < 2 * KS; ++q) s0r[q] = src[4 * q];
+    for (int st = 0; st < CT; ++st) {
+        const float4* src =
+            reinterpret_cast<const float4*>(a.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + col0 + 16 * st + lc) * DK + 4 * lg);
+#pragma unroll
+        for (int q = 0; q < 2 * KS; ++q) s0r[st][q] = src[4 * q];
     }
-    uint2 vr[NTMAX];
+    uint2 vr[CT][NTMAX];
     {
         const uint16_t* vsrc = vg + static_cast<size_t>(b) * N * Hv * DV + static_cast<size_t>(h) * DV + col0 + 4 * lg;
 #pragma unroll
         for (int S = 0; S < NTMAX; ++S)
-            vr[S] = *reinterpret_cast<const uint2*>(vsrc + static_cast<size_t>(min(16 * S + lc, N - 1)) * Hv * DV);
+#pragma unroll
+            for (int st = 0; st < CT; ++st)
+                vr[st][S] = *reinterpret_cast<const uint2*>(vsrc + static_cast<size_t>(min(16 * S + lc, N - 1)) * Hv * DV + 16 * st);
     }
     const int total = w.off[static_cast<size_t>(b) * (N + 1) + N];
     const float* zsrc = w.z + (static_cast<size_t>(b) * Hv + h) * w.P;
     {
-        // the byte arrays as 4-byte words (the pair capacity is a multiple of 4)
-        const uint32_t* ps = reinterpret_cast<const uint32_t*>(w.path + static_cast<size_t>(b) * w.P);
-        const uint32_t* ns = reinterpret_cast<const uint32_t*>(w.pnode + static_cast<size_t>(b) * w.P);
-        const int words = (total + 3) >> 2;
-        for (int e = tid; e < words; e += NTH) {
-            reinterpret_cast<uint32_t*>(smem + L::PATH)[e] = ps[e];
-            reinterpret_cast<uint32_t*>(smem + L::PNODE)[e] = ns[e];
-        }
+        // each pair's place in its tile's blocks, as 4-byte words (the pair
+        // capacity is a multiple of 2), and the first pair of every node
+        const uint32_t* zs = reinterpret_cast<const uint32_t*>(w.zoff + static_cast<size_t>(b) * w.P);
+        const int words = (total + 1) >> 1;
+        for (int e = tid; e < words; e += NTH) reinterpret_cast<uint32_t*>(smem + L::ZOFF)[e] = zs[e];
         for (int i = tid; i <= NMAX; i += NTH) offs[i] = w.off[static_cast<size_t>(b) * (N + 1) + min(i, N)];
     }
-    float gm = 0.f;
-    if (tid < NMAX && tid < N) gm = w.gam[(static_cast<size_t>(b) * Hv + h) * N + tid];
+    for (int i = tid; i < NMAX; i += NTH) gam[i] = i < N ? w.gam[(static_cast<size_t>(b) * Hv + h) * N + i] : 0.f;
 
     // Natural 16-byte chunk c of K or Q row `row` into a buffer in the
     // k-slot order the fragments read: element 32 ks + 16 hh + 4 g + r at
@@ -556,7 +583,6 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
             }
         }
     }
-    if (tid < NMAX) gam[tid] = gm;
 
     // ---- (2) R' = V - gamma o (K S0^T) on MFMA, S0 as bf16 hi + lo; R' kept
     // as fragments (k = node) of the Z~ R' product
@@ -564,45 +590,58 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
     s16x4 eye;   // identity for the V transposes: lane (n, g) holds B[4 g + j][n]
 #pragma unroll
     for (int q = 0; q < 4; ++q) eye[q] = 4 * lg + q == lc ? static_cast<short>(0x3F80) : short(0);
-    bf16x8 s0h[KS], s0l[KS];
+    bf16x8 s0h[CT][KS], s0l[CT][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const float4 x0 = s0r[2 * ks], x1 = s0r[2 * ks + 1];
-        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        split8(x, s0h[ks], s0l[ks]);
-    }
+    for (int st = 0; st < CT; ++st)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const float4 x0 = s0r[st][2 * ks], x1 = s0r[st][2 * ks + 1];
+            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            split8(x, s0h[st][ks], s0l[st][ks]);
+        }
     __syncthreads();
     GDN_SPLIT_PHASE(1);
-    bf16x8 rh[NKMAX], rl[NKMAX];
+    bf16x8 rh[CT][NKMAX], rl[CT][NKMAX];
 #pragma unroll
     for (int kap = 0; kap < NKMAX; ++kap) {
-        float rt[8];
+        float rt[CT][8];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int S = 2 * kap + half;
             if (S < NT) {
-                f32x4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+                f32x4 ah[CT], al[CT];
+#pragma unroll
+                for (int st = 0; st < CT; ++st) ah[st] = al[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int row = 16 * S + lc;
                     const bf16x8 fa = load_frag(KQb + row * (DK * 2) + (((4 * ks + lg) ^ (row & (CH - 1))) << 4));
-                    ah = mfma(fa, s0h[ks], ah);
-                    al = mfma(fa, s0l[ks], al);
+#pragma unroll
+                    for (int st = 0; st < CT; ++st) {
+                        ah[st] = mfma(fa, s0h[st][ks], ah[st]);
+                        al[st] = mfma(fa, s0l[st][ks], al[st]);
+                    }
                 }
                 const f32x4 gq = *reinterpret_cast<const f32x4*>(gam + 16 * S + 4 * lg);
-                const f32x4 vt = mfma16(__builtin_bit_cast(s16x4, vr[S]), eye, f32x4{0.f, 0.f, 0.f, 0.f});
-                const f32x4 pk = ah + al;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const float vv = 16 * S + 4 * lg + rr < N ? vt[rr] : 0.f;
-                    rt[4 * half + rr] = vv - gq[rr] * pk[rr];
+                for (int st = 0; st < CT; ++st) {
+                    const f32x4 vt = mfma16(__builtin_bit_cast(s16x4, vr[st][S]), eye, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 pk = ah[st] + al[st];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const float vv = 16 * S + 4 * lg + rr < N ? vt[rr] : 0.f;
+                        rt[st][4 * half + rr] = vv - gq[rr] * pk[rr];
+                    }
                 }
             } else {
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) rt[4 * half + rr] = 0.f;
+                for (int st = 0; st < CT; ++st)
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) rt[st][4 * half + rr] = 0.f;
             }
         }
-        split8(rt, rh[kap], rl[kap]);
+#pragma unroll
+        for (int st = 0; st < CT; ++st) split8(rt[st], rh[st][kap], rl[st][kap]);
     }
     GDN_SPLIT_PHASE(2);
 
@@ -615,8 +654,6 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
     // and Q rows come from global memory one step ahead of their stage.
     // Block kap of a stage holds nodes 32 kap..; node t of row i sits in lane
     // group ((t >> 2) & 3), slot 4 ((t >> 4) & 1) + (t & 3).
-    const uint8_t* pathc = smem + L::PATH;
-    const uint8_t* pnode = smem + L::PNODE;
     auto zt = [&](int I) { return smem + L::ZT + L::ZT_BYTES * (I % 3); };
     auto qt = [&](int I) { return smem + L::QT + 32 * DK * (I % 3); };
     static_assert(16 * CH <= NTH, "one Q piece per thread");
@@ -629,7 +666,8 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
         const uint32_t row = min(16 * I + t / CH, N - 1);
         return *reinterpret_cast<const uint4*>(qb + row * static_cast<uint32_t>(Hk * DK) + 8u * (t % CH));
     };
-    // the pairs of tile I that thread t scatters (p = -1: none)
+    // the pairs of tile I that thread t scatters (p = -1: none) and their values
+    const uint16_t* zoffs = reinterpret_cast<const uint16_t*>(smem + L::ZOFF);
     auto load_z = [&](int I, int t, int (&p)[TP], float (&zz)[TP]) {
         const int p0 = I < NT ? offs[16 * I] : total;
         const int p1 = I < NT ? offs[min(16 * I + 16, N)] : total;
@@ -645,13 +683,11 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
 #pragma unroll
         for (int u = 0; u < TP; ++u) {
             if (p[u] >= 0) {
-                const int i = pnode[p[u]], tn = pathc[p[u]];
+                const int zo = zoffs[p[u]];
                 const __bf16 zh = static_cast<__bf16>(zz[u]);
                 const __bf16 zl = static_cast<__bf16>(zz[u] - static_cast<float>(zh));
-                const int el = (((((tn >> 2) & 3) << 4) | (i & 15)) << 3) + (((tn >> 4) & 1) << 2) + (tn & 3);
-                unsigned char* blk = Zt + 2048 * (tn >> 5);
-                reinterpret_cast<__bf16*>(blk)[el] = zh;
-                reinterpret_cast<__bf16*>(blk + 1024)[el] = zl;
+                *reinterpret_cast<__bf16*>(Zt + zo) = zh;
+                *reinterpret_cast<__bf16*>(Zt + zo + 1024) = zl;
             }
         }
     };
@@ -659,13 +695,16 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
         const int nb = I / 2 + 1;
         for (int e = tid; e < nb * 128; e += NTH) reinterpret_cast<uint4*>(zt(I))[e] = make_uint4(0u, 0u, 0u, 0u);
     };
-    // o is written once: plain stores, whose two 64-byte halves of each
-    // 128-byte row piece (from the two wavefronts of one SIMD) meet in L2
-    auto store_o = [&](int I, int ln, const f32x4& v) {
+    // o is written once: plain stores (the 64-byte pieces of one 128-byte
+    // row piece meet in L2)
+    auto store_o = [&](int I, int ln, const f32x4 (&v)[CT]) {
         const int i = 16 * I + (ln & 15);
-        if (i < N)
-            *reinterpret_cast<f32x4*>(ob + (static_cast<uint32_t>(i) * static_cast<uint32_t>(Hv * DV) +
-                                            static_cast<uint32_t>(col0 + 4 * (ln >> 4)))) = v;
+        if (i < N) {
+#pragma unroll
+            for (int st = 0; st < CT; ++st)
+                *reinterpret_cast<f32x4*>(ob + (static_cast<uint32_t>(i) * static_cast<uint32_t>(Hv * DV) +
+                                                static_cast<uint32_t>(col0 + 16 * st + 4 * (ln >> 4)))) = v[st];
+        }
     };
 
     __syncthreads();   // K is no longer read
@@ -684,7 +723,9 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
     // wait for the prefetched rows: loads and stores share one wait counter,
     // so a wait for a load also waits for stores issued before it, and this
     // keeps those stores a whole tile old.
-    f32x4 prev = {0.f, 0.f, 0.f, 0.f};
+    f32x4 prev[CT];
+#pragma unroll
+    for (int st = 0; st < CT; ++st) prev[st] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int I = 0; I < NT; ++I) {
         // lane indices through an opaque copy: offsets derived from them are
         // formed per tile instead of held in registers
@@ -698,15 +739,22 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
             qv = load_q(min(I + 2, NT - 1), t);
             load_z(I + 2, t, pn, zv);
         }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[CT];
+#pragma unroll
+        for (int st = 0; st < CT; ++st) acc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
         const unsigned char* Qt = qt(I);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 fb = load_frag(Qt + c16 * (DK * 2) + (((4 * ks + (ln >> 4)) ^ (c16 & (CH - 1))) << 4));
-            acc = mfma(s0h[ks], fb, acc);
-            acc = mfma(s0l[ks], fb, acc);
+#pragma unroll
+            for (int st = 0; st < CT; ++st) {
+                acc[st] = mfma(s0h[st][ks], fb, acc[st]);
+                acc[st] = mfma(s0l[st][ks], fb, acc[st]);
+            }
         }
-        acc *= gam[16 * I + c16];
+        const float gi = gam[16 * I + c16];
+#pragma unroll
+        for (int st = 0; st < CT; ++st) acc[st] *= gi;
         const unsigned char* blk = zt(I) + 16 * ln;
         const int nb = I / 2 + 1;
 #pragma unroll
@@ -714,12 +762,16 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void dense_kernel(VerifyArgs 
             if (kap < nb) {
                 const bf16x8 zh = load_frag(blk + 2048 * kap);
                 const bf16x8 zl = load_frag(blk + 2048 * kap + 1024);
-                acc = mfma(rh[kap], zh, acc);
-                acc = mfma(rl[kap], zh, acc);
-                acc = mfma(rh[kap], zl, acc);
+#pragma unroll
+                for (int st = 0; st < CT; ++st) {
+                    acc[st] = mfma(rh[st][kap], zh, acc[st]);
+                    acc[st] = mfma(rl[st][kap], zh, acc[st]);
+                    acc[st] = mfma(rh[st][kap], zl, acc[st]);
+                }
             }
         }
-        prev = acc;
+#pragma unroll
+        for (int st = 0; st < CT; ++st) prev[st] = acc[st];
         if (I + 2 < NT) zero(I + 2);
     }
     store_o(NT - 1, lane, prev);
@@ -732,7 +784,10 @@ hipError_t launch_split_t(const VerifyArgs& a, const SplitWs& w, hipStream_t str
     hipLaunchKernelGGL((tree_kernel<NMAX, DK>), dim3(static_cast<unsigned>(a.B) * a.H_k), dim3(2 * NMAX), 0, stream, a, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dense_kernel<NMAX, DK, DV>), dim3(static_cast<unsigned>(a.B) * a.H_v), dim3(4 * DV), 0, stream, a, w);
+    // two column tiles per wavefront at d_v = 128 (4 wavefronts), one at 64
+    constexpr int CT = DV == 128 ? 2 : 1;
+    hipLaunchKernelGGL((dense_kernel<NMAX, DK, DV, CT>), dim3(static_cast<unsigned>(a.B) * a.H_v), dim3(4 * DV / CT), 0,
+                       stream, a, w);
     return hipGetLastError();
 }
 
