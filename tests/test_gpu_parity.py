@@ -503,8 +503,10 @@ def test_pair_list_capacity_boundary(N, spines, expect):
     """trees whose paths sum to the most a best-first tree of the pages'
     depth reaches (1928 nodes at N = 128, depth 16; 5868 at N = 256, depth
     24), to the pair-list capacity of the MFMA kernels (2048, 6144) and one
-    past it, between best-first trees: the first two stay on the MFMA path,
-    the last takes the per-node walk"""
+    past it, between best-first trees.  At N = 128 the first two stay on the
+    MFMA path and the last takes the per-node walk; at N = 256 the
+    two-launch verify solves root paths of up to 24 nodes, so the first
+    stays on the MFMA path and the other two (depth 26) are walked"""
     cfg = G.shrink(G.CONFIGS["bestfirst_b32n128"], B=6, N=N, H_k=2, H_v=4)
     inp = G.make_inputs(cfg, seed=5)
     par = inp["parent"].copy()
