@@ -141,9 +141,28 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
     uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + L::TMASK);
     int* misc = reinterpret_cast<int*>(smem + L::MISC);
 
-    // ---- (1) Q rows of this wavefront's Gram row tiles (held in registers
-    // through the structure phases), parents, g and beta of the first two
-    // value heads, K
+    // ---- (1) parents, g and beta of the first two value heads (which the
+    // structure phases wait for, so they are issued first), then the Q rows
+    // of this wavefront's Gram row tiles and the K rows, held in registers
+    // through the structure phases
+    int p = -1;
+    if (tid < NMAX && tid < N) p = a.parent[static_cast<size_t>(b) * N + tid];
+    auto load_gb = [&](int r0, float& gi, float& bi) {
+        const int r = r0 + hr;
+        gi = 0.f;
+        bi = 0.f;
+        if (r < R && ni < N) {
+            const size_t nh = (static_cast<size_t>(b) * N + ni) * Hv + kh * R + r;
+            gi = a.g[nh];
+            bi = a.beta[nh];
+        }
+    };
+    auto store_gb = [&](float gi, float bi) {
+        gv[hr * NMAX + ni] = gi;
+        bet[hr * NMAX + ni] = bi;
+    };
+    float g0, b0;
+    load_gb(0, g0, b0);
     auto row_tile = [&](int u) { return u == 0 ? wave : 2 * NW - 1 - wave; };
     bf16x8 qa[RU][KS];
 #pragma unroll
@@ -152,36 +171,16 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
         for (int ks = 0; ks < KS; ++ks)
             qa[u][ks] = load_frag(qg + ((static_cast<size_t>(b) * N + min(16 * row_tile(u) + lc, N - 1)) * Hk + kh) * DK +
                                   8 * KS * lg + 8 * ks);
-    int p = -1;
-    if (tid < NMAX && tid < N) p = a.parent[static_cast<size_t>(b) * N + tid];
-    auto load_gb = [&](int r0) {
-        const int r = r0 + hr;
-        float gi = 0.f, bi = 0.f;
-        if (r < R && ni < N) {
-            const size_t nh = (static_cast<size_t>(b) * N + ni) * Hv + kh * R + r;
-            gi = a.g[nh];
-            bi = a.beta[nh];
-        }
-        gv[hr * NMAX + ni] = gi;
-        bet[hr * NMAX + ni] = bi;
-    };
-    load_gb(0);
-    {
-        uint4 kv[KCH];
+    // K rows: loaded now, written to LDS after the structure phases, which
+    // their latency overlaps
+    uint4 kv[KCH];
 #pragma unroll
-        for (int q = 0; q < KCH; ++q) {
-            const int e = tid + q * NTH;
-            const int row = min(e / (DK / 8), N - 1);
-            kv[q] = *reinterpret_cast<const uint4*>(kg + ((static_cast<size_t>(b) * N + row) * Hk + kh) * DK + (e % (DK / 8)) * 8);
-        }
-#pragma unroll
-        for (int q = 0; q < KCH; ++q) {
-            const int e = tid + q * NTH;
-            const int row = e / (DK / 8), cc = e % (DK / 8);
-            const uint4 v = row < N ? kv[q] : make_uint4(0u, 0u, 0u, 0u);
-            *reinterpret_cast<uint4*>(Ks + row * L::KROW + cc * 16) = v;
-        }
+    for (int q = 0; q < KCH; ++q) {
+        const int e = tid + q * NTH;
+        const int row = min(e / (DK / 8), N - 1);
+        kv[q] = *reinterpret_cast<const uint4*>(kg + ((static_cast<size_t>(b) * N + row) * Hk + kh) * DK + (e % (DK / 8)) * 8);
     }
+    store_gb(g0, b0);
     int bad_local = 0;
     if (tid < NMAX) {
         const int i = tid;
@@ -249,6 +248,13 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
     }
     __syncthreads();
     const int total = misc[0];
+#pragma unroll
+    for (int q = 0; q < KCH; ++q) {
+        const int e = tid + q * NTH;
+        const int row = e / (DK / 8), cc = e % (DK / 8);
+        const uint4 v = row < N ? kv[q] : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(Ks + row * L::KROW + cc * 16) = v;
+    }
     if (tid < NMAX && tid < N) {
         // node i's root path, root first, at its pairs; the tiles that hold
         // pairs; (key head 0) where each pair's entry goes in the dense
@@ -363,7 +369,9 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
     for (int r0 = 0; r0 < R; r0 += 2) {
         if (r0 > 0) {
             __syncthreads();   // the previous pair's reads of gv, bet, Gs and X are done
-            load_gb(r0);
+            float gi, bi;
+            load_gb(r0, gi, bi);
+            store_gb(gi, bi);
             __syncthreads();
         }
         const int r = r0 + hr;
