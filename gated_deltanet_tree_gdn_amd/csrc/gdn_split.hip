@@ -674,15 +674,20 @@ __global__ __launch_bounds__(4 * DV / CT, 2) void dense_kernel(VerifyArgs a, Spl
         const uint32_t row = min(16 * I + t / CH, N - 1);
         return *reinterpret_cast<const uint4*>(qb + row * static_cast<uint32_t>(Hk * DK) + 8u * (t % CH));
     };
-    // the pairs of tile I that thread t scatters (p = -1: none) and their values
+    // the pairs of tile I that thread t scatters, read a tile ahead: each
+    // one's place in the tile's blocks (-1: none) and its value.  (The pair
+    // range comes from LDS: a global load waited on here would also wait
+    // for the o stores in flight.)
     const uint16_t* zoffs = reinterpret_cast<const uint16_t*>(smem + L::ZOFF);
     auto load_z = [&](int I, int t, int (&p)[TP], float (&zz)[TP]) {
         const int p0 = I < NT ? offs[16 * I] : total;
         const int p1 = I < NT ? offs[min(16 * I + 16, N)] : total;
 #pragma unroll
         for (int u = 0; u < TP; ++u) {
-            p[u] = p0 + t + u * NTH < p1 ? p0 + t + u * NTH : -1;
-            zz[u] = zsrc[static_cast<uint32_t>(p[u] >= 0 ? p[u] : 0)];
+            const bool has = p0 + t + u * NTH < p1;
+            const int e = has ? p0 + t + u * NTH : 0;
+            zz[u] = zsrc[static_cast<uint32_t>(e)];
+            p[u] = has ? static_cast<int>(zoffs[e]) : -1;
         }
     };
     auto fill = [&](int I, int t, const uint4& qv, const int (&p)[TP], const float (&zz)[TP]) {
@@ -691,11 +696,10 @@ __global__ __launch_bounds__(4 * DV / CT, 2) void dense_kernel(VerifyArgs a, Spl
 #pragma unroll
         for (int u = 0; u < TP; ++u) {
             if (p[u] >= 0) {
-                const int zo = zoffs[p[u]];
                 const __bf16 zh = static_cast<__bf16>(zz[u]);
                 const __bf16 zl = static_cast<__bf16>(zz[u] - static_cast<float>(zh));
-                *reinterpret_cast<__bf16*>(Zt + zo) = zh;
-                *reinterpret_cast<__bf16*>(Zt + zo + 1024) = zl;
+                *reinterpret_cast<__bf16*>(Zt + p[u]) = zh;
+                *reinterpret_cast<__bf16*>(Zt + p[u] + 1024) = zl;
             }
         }
     };

@@ -483,6 +483,26 @@ def test_pipeline_item_boundaries(shape):
     assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), f"pipeline {shape} o")
 
 
+def test_workspace_reused_across_trees():
+    """trees of more than 128 nodes go through the context's workspace (the
+    pair structure, per-sequence deep flags and the values of Z~): three
+    verifies on one context, deep and shallow sequences swapping places
+    between calls, each against the oracle"""
+    cfg = G.shrink(G.CONFIGS["bestfirst_b32n128"], B=4, N=200, H_k=2, H_v=4)
+    ctx = None
+    for call, chain_every in enumerate((2, 3, 1000)):
+        inp = _mixed_depth_inputs(cfg, seed=40 + call, chain_every=chain_every)
+        if chain_every == 3:
+            # the sequences that were deep in the first call are shallow now
+            inp["parent"][[0, 2]] = G.make_inputs(cfg, seed=50)["parent"][[0, 2]]
+            inp["parent"][1] = np.arange(-1, cfg.N - 1, dtype=np.int32)
+        d = G.to_device(inp)
+        say(f"[workspace] call {call + 1}")
+        o, ctx = run_verify(d, ctx)
+        gdn.gdn_ctx_status(ctx)
+        assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), f"workspace call {call + 1} o")
+
+
 def _spine_tree(N, k, extra):
     """a chain of k nodes, every other node a child of the chain's last
     node, and the last `extra` of those one level deeper (under node k):
