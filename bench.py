@@ -45,10 +45,15 @@ def traffic_file(workload):
 
 
 def kernel_source_sha() -> str:
+    """Hash of the kernel sources' code: line comments and blank lines are
+    left out, so that a comment edit keeps the counters taken on the code."""
     h = hashlib.sha256()
     for s in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "gated_deltanet_tree_gdn_amd", "csrc", s), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "gated_deltanet_tree_gdn_amd", "csrc", s), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -31,8 +31,8 @@
 // overlaps one item's tree side with another's dense side, is faster.)
 //
 // Workspace (per context, written by the tree kernel, read by the dense
-// kernel), with P = N ZR pairs per sequence at most (ZR = 16 for N <= 128,
-// 24 above):
+// kernel), with P = 24 N pairs per sequence at most (root paths of up to
+// ZR = 24 nodes):
 //   z     float [B][H_v][P]  Z~ values in pair order (below), times beta of
 //                            the ancestor
 //   gam   float [B][H_v][N]  gamma
@@ -67,7 +67,6 @@ namespace {
 __host__ __device__ constexpr int sp_align(int x, int a) { return (x + a - 1) / a * a; }
 __host__ __device__ constexpr int sp_max(int x, int y) { return x > y ? x : y; }
 __host__ __device__ constexpr int sp_zr(int n) { return n > 128 ? 24 : 16; }
-
 
 // ---------------------------------------------------------------- tree kernel
 
@@ -197,7 +196,7 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
     GDN_SPLIT_PHASE(1);
 
     // ---- (2) structure: depth by pointer jumping (dep[i] counts the nodes
-    // from i up to nxt[i]), pair offsets, root paths, ancestor bits
+    // from i up to nxt[i]), pair offsets, root paths, the tiles holding pairs
     for (int round = 0; round < 9; ++round) {
         int c2 = 0, n2 = -1;
         if (tid < NMAX) {
