@@ -90,7 +90,11 @@ typedef struct {
 typedef struct gdn_ctx gdn_ctx;
 
 /* Bytes of device workspace a context for `dims` needs (a multiple of 256;
- * holds the per-sequence tree / accepted verdicts).  0 if dims is NULL. */
+ * holds the per-sequence tree / accepted verdicts and, for N > 128, the
+ * verify's intermediate between its two launches: per (sequence, value head)
+ * the values of the tree-shaped operator on the ancestor pairs and gamma, per
+ * sequence where each pair goes, about 4 (24 N + N) H_v B + 4 N B bytes).
+ * 0 if dims is NULL. */
 size_t gdn_tree_workspace_bytes(const gdn_tree_dims* dims);
 
 /* Creates a context for `dims` over a caller-owned device workspace of at

@@ -58,6 +58,20 @@ def test_workspace_bytes(lib):
     assert lib.gdn_tree_workspace_bytes(None) == 0
 
 
+@pytest.mark.parametrize("B,N,H_v", [(64, 256, 32), (3, 129, 4), (1, 200, 1)])
+def test_workspace_holds_the_two_launch_intermediate(lib, B, N, H_v):
+    """trees of more than 128 nodes: the verdict words plus, per (sequence,
+    value head), 24 N pair values and N gammas, and per sequence a 2-byte
+    place per pair and N + 1 offsets; trees of at most 128 nodes: only the
+    verdict words"""
+    d = dims(B=B, N=N, H_k=1, H_v=H_v)
+    n = lib.gdn_tree_workspace_bytes(ctypes.byref(d))
+    need = 8 * B + 4 * (24 * N + N) * H_v * B + 2 * 24 * N * B + 4 * (N + 1) * B + 4 * B
+    assert n % 256 == 0 and need <= n <= need + 8 * 256
+    small = dims(B=B, N=128, H_k=1, H_v=H_v)
+    assert lib.gdn_tree_workspace_bytes(ctypes.byref(small)) == max(256, -(-8 * B // 256) * 256)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(N=257), "GDN_ERR_SHAPE"), (dict(N=-1), "GDN_ERR_SHAPE"), (dict(B=-3), "GDN_ERR_SHAPE"),
     (dict(H_v=3), "GDN_ERR_SHAPE"), (dict(H_k=0), "GDN_ERR_SHAPE"), (dict(d_k=96), "GDN_ERR_SHAPE"),
