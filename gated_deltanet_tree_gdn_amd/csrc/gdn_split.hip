@@ -18,7 +18,7 @@
 //     O = gamma o (Q S0^T) + Z~ R'.
 //
 // Why two launches: at this size one item's tree side (structure, Gram of
-// the ancestor pairs, X and Y, the row solve) is a long chain of dependent
+// the ancestor pairs, the row solve) is a long chain of dependent
 // phases, and an item's dense side needs most of a compute unit's LDS and
 // registers, so the two cannot share a workgroup without running in turn.
 // Here the tree kernel runs the chains of the whole batch side by side, one
@@ -76,10 +76,13 @@ struct TreeLds {
     static constexpr int CAP = NMAX * ZR;
     static constexpr int KROW = DK * 2 + 16;             // staged k row, padded against bank conflicts
     static constexpr int KS_BYTES = NMAX * KROW;
-    static constexpr int XH = CAP + 32;                  // X of one value head (32 zero pads)
-    static constexpr int KS = 0;                         // K rows; after the Gram, X of two value heads
-    static constexpr int KK = sp_align(sp_max(KS_BYTES, 2 * 4 * XH), 16);  // float[CAP + 4]: k_i . k_s
-    static constexpr int QK = KK + 4 * (CAP + 4);        // float[CAP + 4]: q_i . k_s
+    static constexpr int KS = 0;                         // K rows
+    // float[CAP + 4 + 32]: k_i . k_s; entry CAP takes the Gram tile entries
+    // that are not pairs, entries KZERO .. KZERO + 31 stay zero (the row the
+    // solve reads for path positions past a node's depth)
+    static constexpr int KK = sp_align(KS_BYTES, 16);
+    static constexpr int KZERO = CAP + 4;
+    static constexpr int QK = KK + 4 * (CAP + 4 + 32);   // float[CAP + 4]: q_i . k_s
     static constexpr int PATH = QK + 4 * (CAP + 4);      // uint8[CAP]: ancestor of each pair
     static constexpr int NODE = sp_align(PATH + CAP, 16);
     static constexpr int PAR = NODE;                     // int[NMAX]
@@ -126,7 +129,6 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
     const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
 
     unsigned char* Ks = smem + L::KS;
-    float* xcb = reinterpret_cast<float*>(smem + L::KS);
     float* kk = reinterpret_cast<float*>(smem + L::KK);
     float* qk = reinterpret_cast<float*>(smem + L::QK);
     uint8_t* pathc = smem + L::PATH;
@@ -192,6 +194,7 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
         dep[i] = i < N ? 1 : 0;
     }
     if (tid < NTMAX) tmask[tid] = 0u;
+    if (tid >= 64 && tid < 64 + 32) kk[L::KZERO + tid - 64] = 0.f;
     const int bad = __syncthreads_or(bad_local);
     GDN_SPLIT_PHASE(1);
 
@@ -360,14 +363,18 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
             }
         }
     }
-    __syncthreads();   // K is no longer read: its area holds X from here on
+    __syncthreads();
     GDN_SPLIT_PHASE(4);
 
-    // ---- (4) per pair of value heads: G, gamma; X; rows of Z~
-    float* xh = xcb + hr * L::XH;
+    // ---- (4) per pair of value heads: G, gamma; rows of Z~.  Along node i's
+    // root path t_0 (root) .. t_{m-1} = i the row w of Y (I + X)^-1 solves
+    // w_b = Y_{i,t_b} - sum_{a > b} w_a X_{t_a,t_b}.  As D_{i,t_a} D_{t_a,t_b} =
+    // D_{i,t_b}, w_b = D_{i,t_b} y_b with
+    //     y_b = q_i . k_{t_b} - sum_{a > b} (beta_{t_a} y_a) (k_{t_a} . k_{t_b}),
+    // a sweep over the Gram values and beta only; Z~_{i,t_b} = beta_{t_b} w_b.
     for (int r0 = 0; r0 < R; r0 += 2) {
         if (r0 > 0) {
-            __syncthreads();   // the previous pair's reads of gv, bet, Gs and X are done
+            __syncthreads();   // the previous pair's reads of gv, bet and Gs are done
             float gi, bi;
             load_gb(r0, gi, bi);
             store_gb(gi, bi);
@@ -378,48 +385,43 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
         const int h = kh * R + r;
         const int o = off[ni], m = live ? dep[ni] : 0;
         const float* gvh = gv + hr * NMAX;
+        const float* bh = bet + hr * NMAX;
         float* Gh = Gs + hr * NMAX;
-        int t[ZR];
-#pragma unroll
-        for (int d = 0; d < ZR; ++d) t[d] = min(static_cast<int>(pathc[min(o + min(d, max(m - 1, 0)), L::CAP - 1)]), NMAX - 1);
+        auto path_at = [&](int d) {
+            return min(static_cast<int>(pathc[min(o + min(d, max(m - 1, 0)), L::CAP - 1)]), NMAX - 1);
+        };
         float G = 0.f;
 #pragma unroll
-        for (int d = 0; d < ZR; ++d) G += d < m ? gvh[t[d]] : 0.f;
+        for (int d = 0; d < ZR; ++d) G += d < m ? gvh[path_at(d)] : 0.f;
         Gh[ni] = G;
         if (live) w.gam[(static_cast<size_t>(b) * Hv + h) * N + ni] = __expf(G);
         __syncthreads();
         GDN_SPLIT_PHASE(5);
-        // X row of node ni (root first; the last entry, i itself, is not used)
-        const float bi = bet[hr * NMAX + ni];
-#pragma unroll
-        for (int d = 0; d < ZR; ++d)
-            if (d < m) xh[o + d] = bi * __expf(G - Gh[t[d]]) * kk[o + d];
-        if (ni < 32) xh[total + ni] = 0.f;   // pads read by the branch-free solve
-        __syncthreads();
         GDN_SPLIT_PHASE(6);
         if (live) {
-            // z (I + X) = y along the root path t_0 (root) .. t_{m-1} = i,
-            // swept from the node end: once z_a is final, z_b -= z_a X_{t_a, t_b}
-            // for b < a, X_{t_a, t_b} at position b of t_a's row.  Entries
-            // past the path are zero and their X reads land on finite values.
+            // swept from the node end: once y_a is final, y_b -= beta_{t_a} y_a
+            // (k_{t_a} . k_{t_b}) for b < a, the Gram value at position b of
+            // t_a's root path; positions past the path read the zero row
             int oa[ZR];
-            float z[ZR];
+            float y[ZR], bt[ZR];
 #pragma unroll
             for (int d = 0; d < ZR; ++d) {
-                oa[d] = off[t[d]];
-                z[d] = d < m ? __expf(G - Gh[t[d]]) * qk[o + d] : 0.f;
+                const int t = path_at(d);
+                oa[d] = d < m ? off[t] : L::KZERO;
+                bt[d] = bh[t];
+                y[d] = d < m ? qk[o + d] : 0.f;
             }
             float xr[ZR - 1];
 #pragma unroll
-            for (int e = 0; e < ZR - 1; ++e) xr[e] = xh[oa[ZR - 1] + e];
+            for (int e = 0; e < ZR - 1; ++e) xr[e] = kk[oa[ZR - 1] + e];
 #pragma unroll
             for (int aa = ZR - 1; aa >= 1; --aa) {
                 float xn[ZR - 1];
 #pragma unroll
-                for (int e = 0; e + 1 < aa; ++e) xn[e] = xh[oa[aa - 1] + e];
-                const float za = z[aa];
+                for (int e = 0; e + 1 < aa; ++e) xn[e] = kk[oa[aa - 1] + e];
+                const float ya = y[aa] * bt[aa];
 #pragma unroll
-                for (int e = 0; e < aa; ++e) z[e] -= za * xr[e];
+                for (int e = 0; e < aa; ++e) y[e] -= ya * xr[e];
 #pragma unroll
                 for (int e = 0; e + 1 < aa; ++e) xr[e] = xn[e];
                 __builtin_amdgcn_sched_barrier(0);
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
             float* zg = w.z + (static_cast<size_t>(b) * Hv + h) * w.P + o;
 #pragma unroll
             for (int d = 0; d < ZR; ++d)
-                if (d < m) zg[d] = z[d] * bet[hr * NMAX + t[d]];
+                if (d < m) zg[d] = y[d] * bt[d] * __expf(G - Gh[path_at(d)]);
         }
     }
     GDN_SPLIT_PHASE(7);

@@ -19,7 +19,7 @@
 //    values k_i . k_s and q_i . k_s of the pairs (MFMA; K and Q of the key
 //    head sit in these wavefronts' registers, two row tiles each, and four
 //    column tiles at a time are broadcast through LDS); the gates G, gamma;
-//    X and Y; the rows of Z~.  Results go to one of two LDS slots.  The same
+//    the rows of Z~.  Results go to one of two LDS slots.  The same
 //    K/Q registers are written to LDS, in the dense side's fragment order,
 //    when the dense side moves to the new key head;
 //  - dense wavefronts finish item j meanwhile: its Z~ (from the other slot)
@@ -88,11 +88,14 @@ struct WsLds {
     static constexpr int S_GAM = 4 * CAP;
     static constexpr int SLOTS_END = SLOTS + 2 * SLOT;
     // tree side
-    static constexpr int XC = ws_align(SLOTS_END, 16);  // float[CAP + 16]: X (zero pads)
-    // float[CAP + 4]: k_i . k_s and q_i . k_s per key head (entry CAP takes
-    // the Gram tile entries that are not ancestor pairs)
-    static constexpr int KK = XC + 4 * (CAP + 16);
-    static constexpr int QK = KK + 4 * (CAP + 4);
+    // k_i . k_s (float[CAP + 4 + 16]) and q_i . k_s (float[CAP + 4]) per key
+    // head: entry CAP takes the Gram tile entries that are not ancestor
+    // pairs; entries CAP + 4 .. CAP + 19 of k_i . k_s stay zero (the row the
+    // solve reads for path positions past a node's depth)
+    static constexpr int GB0 = ws_align(SLOTS_END, 16);
+    static constexpr int KK = GB0 + 32 * DK;
+    static constexpr int KZERO = CAP + 4;
+    static constexpr int QK = KK + 4 * (CAP + 4 + 16);
     static constexpr int PATH = QK + 4 * (CAP + 4);  // uint8[CAP]: the root..i path of every node i
     static constexpr int PNODE = PATH + CAP;         // uint8[CAP]: node i owning each pair
     static constexpr int NODE = ws_align(PNODE + CAP, 16);
@@ -107,13 +110,11 @@ struct WsLds {
     static constexpr int TMASK = ANC + 4 * AW * NMAX;
     static constexpr int MISC = TMASK + 4 * (NMAX / 16);  // int[16]
     // Gram broadcast of 16-row tiles of K (KS fragments x 64 lanes x 16
-    // bytes each), four at a time: buffer 0 overlays X (free until X is
-    // built), 1 is its own, 2 and 3 overlay the hand-over slot of the item
-    // being built (free until its Y is written)
+    // bytes each), four at a time: buffers 0 and 1 are their own, 2 and 3
+    // overlay the hand-over slot of the item being built (free until its
+    // rows of Z~ are written)
     static constexpr int GB_BYTES = 32 * DK;
-    static constexpr int GB0 = XC;
     static constexpr int GB1 = MISC + 64;
-    static_assert(GB_BYTES <= 4 * (CAP + 16), "Gram buffer 0 must fit in X");
     static_assert(2 * GB_BYTES <= SLOT, "Gram buffers 2 and 3 must fit in a hand-over slot");
     static constexpr int TOTAL = GB1 + GB_BYTES;
     // misc[]: 0 tree total, 2 dense sync counter, 3 tree sync counter,
@@ -223,7 +224,6 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
     auto slot_base = [&](int sl) { return smem + L::SLOTS + sl * L::SLOT; };
     auto zout_s = [&](int sl) { return reinterpret_cast<float*>(slot_base(sl)); };
     auto gamd_s = [&](int sl) { return reinterpret_cast<float*>(slot_base(sl) + L::S_GAM); };
-    float* xc = reinterpret_cast<float*>(smem + L::XC);
     float* kk = reinterpret_cast<float*>(smem + L::KK);
     float* qk = reinterpret_cast<float*>(smem + L::QK);
     uint8_t* pathc = smem + L::PATH;
@@ -568,62 +568,66 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
         }
         t_kh = item_kh(j);
     };
-    // X and Y, the rows of Z~, the pair positions
+    // The rows of Z~.  With D_is = exp(G_i - G_s), the row w of node i in
+    // Y (I + X)^-1 satisfies w_b = Y_{i,t_b} - sum_{a > b} w_a X_{t_a,t_b}
+    // along its root path t_0 .. t_{m-1} = i.  Since D_{i,t_a} D_{t_a,t_b} =
+    // D_{i,t_b}, w_b = D_{i,t_b} y_b with
+    //     y_b = q_i . k_{t_b} - sum_{a > b} (beta_{t_a} y_a) (k_{t_a} . k_{t_b}),
+    // so the sweep runs on the Gram values and beta alone (no per-pair gate
+    // factors, no quotient of gates), and Z~_{i,t_b} = y_b beta_{t_b} D_{i,t_b}.
     auto tree_tail = [&](int j) {
         const int slot = j & 1;
-        const int total = t_total;
         tree_sync();
         GDN_PHASE(11);
-        // X and Y per pair
         float* ye = zout_s(slot);
-        for (int p = ttid; p < total; p += TTH) {
-            const int i = pnode[p], s = pathc[p];
-            const float D = __expf(Gs[i] - Gs[s]);
-            xc[p] = bet[i] * D * kk[p];
-            ye[p] = D * qk[p];
-        }
-        if (ttid < 16) xc[total + ttid] = 0.f;  // pads for the solve below
-        tree_sync();
         GDN_PHASE(12);
         // per node its row of Z~ by a right-looking sweep along its path
         if (ttid < N) {
             const int i = ttid;
             const int o = off[i], m = dep[i];
+            const float Gi = Gs[i];
             if (m <= ZR) {
-                int tt[ZR], oa[ZR];
-                float z[ZR];
+                // path positions past the depth read the zero row of kk
+                int oa[ZR];
+                float y[ZR], bt[ZR];
 #pragma unroll
                 for (int bb = 0; bb < ZR; ++bb) {
                     const int pp = o + min(bb, m - 1);
-                    tt[bb] = pathc[pp];
-                    oa[bb] = off[tt[bb]];
-                    z[bb] = bb < m ? ye[pp] : 0.f;
+                    const int t = pathc[pp];
+                    oa[bb] = bb < m ? off[t] : L::KZERO;
+                    bt[bb] = bet[t];
+                    y[bb] = bb < m ? qk[pp] : 0.f;
                 }
                 float xr[ZR - 1];
 #pragma unroll
-                for (int bb = 0; bb < ZR - 1; ++bb) xr[bb] = xc[oa[ZR - 1] + bb];
+                for (int bb = 0; bb < ZR - 1; ++bb) xr[bb] = kk[oa[ZR - 1] + bb];
 #pragma unroll
                 for (int aa = ZR - 1; aa >= 1; --aa) {
                     float xn[ZR - 1];
 #pragma unroll
-                    for (int bb = 0; bb + 1 < aa; ++bb) xn[bb] = xc[oa[aa - 1] + bb];
-                    const float za = z[aa];
+                    for (int bb = 0; bb + 1 < aa; ++bb) xn[bb] = kk[oa[aa - 1] + bb];
+                    const float ya = y[aa] * bt[aa];
 #pragma unroll
-                    for (int bb = 0; bb < aa; ++bb) z[bb] -= za * xr[bb];
+                    for (int bb = 0; bb < aa; ++bb) y[bb] -= ya * xr[bb];
 #pragma unroll
                     for (int bb = 0; bb + 1 < aa; ++bb) xr[bb] = xn[bb];
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
                 for (int bb = 0; bb < ZR; ++bb)
-                    if (bb < m) ye[o + bb] = z[bb] * bet[tt[bb]];
+                    if (bb < m) ye[o + bb] = y[bb] * bt[bb] * __expf(Gi - Gs[pathc[o + bb]]);
             } else {
+                for (int bb = 0; bb < m; ++bb) ye[o + bb] = qk[o + bb];
                 for (int aa = m - 1; aa >= 1; --aa) {
-                    const float za = ye[o + aa];
-                    const int oa = off[pathc[o + aa]];
-                    for (int bb = 0; bb < aa; ++bb) ye[o + bb] -= za * xc[oa + bb];
+                    const int ta = pathc[o + aa];
+                    const float ya = ye[o + aa] * bet[ta];
+                    const int oa = off[ta];
+                    for (int bb = 0; bb < aa; ++bb) ye[o + bb] -= ya * kk[oa + bb];
                 }
-                for (int bb = 0; bb < m; ++bb) ye[o + bb] *= bet[pathc[o + bb]];
+                for (int bb = 0; bb < m; ++bb) {
+                    const int t = pathc[o + bb];
+                    ye[o + bb] *= bet[t] * __expf(Gi - Gs[t]);
+                }
             }
         }
         tree_sync();
@@ -856,6 +860,7 @@ __global__ __launch_bounds__(64 * (NWD + 4)) void verify_ws_kernel(VerifyArgs a,
                                (L::HAS_FALLBACK && misc[7 + (j & 1)]));
     };
     if (tid < 16) misc[tid] = 0;
+    if (tid >= 64 && tid < 64 + 16) kk[L::KZERO + tid - 64] = 0.f;
     __syncthreads();
     // a key head (or sequence) starts at item j: K/Q go into the registers
     auto new_kq_at = [&](int j) {
