@@ -112,10 +112,12 @@ def read_traffic(kernel, workload=WORKLOAD):
 
 COPY_CALLS = 5
 # kernel-name patterns per role; a verify of more than 128 nodes is the
-# tree kernel and then the dense kernel, whose per-launch bytes add up
-KERNELS = {"verify": ("verify_ws_kernel", "verify_fast_kernel"), "verify_tree": ("tree_kernel",),
-           "verify_dense": ("dense_kernel",), "commit": ("commit_mfma_kernel",),
-           "commit_verify": ("commit_verify_kernel",), "copy": ("MulFunctor",)}
+# tree kernel and then the dense kernel, whose per-launch bytes add up; the
+# allocation-free entry point runs the single-launch kernel there
+KERNELS = {"verify": ("verify_ws_kernel",), "verify_tree": ("tree_kernel",),
+           "verify_dense": ("dense_kernel",), "verify_static": ("verify_fast_kernel",),
+           "commit": ("commit_mfma_kernel",), "commit_verify": ("commit_verify_kernel",),
+           "copy": ("MulFunctor",)}
 
 
 def write_traffic(fetch_csv, write_csv, copy_mib, workload):
@@ -145,7 +147,7 @@ def write_traffic(fetch_csv, write_csv, copy_mib, workload):
     out = {"kernel_source_sha": kernel_source_sha(), "copy_kib": copy_kib,
            "fetch_factor": ff, "write_factor": fw, "dispatches": {"fetch": nf, "write": nw}}
     out["workload"] = workload
-    for k in ("verify", "verify_tree", "verify_dense", "commit", "commit_verify"):
+    for k in ("verify", "verify_tree", "verify_dense", "verify_static", "commit", "commit_verify"):
         if fetch[k] is None or write[k] is None:
             continue
         out[k] = {"fetch_kib": fetch[k], "write_kib": write[k],
@@ -294,6 +296,10 @@ def main():
     def commit(s):
         gdn.gdn_commit_path(s["ctx"], s["accepted"], S_new=s["S_new"], stream=stream)
 
+    def verify_static(s):
+        gdn.gdn_tree_verify_static(s["q"], s["k"], s["v"], s["g"], s["beta"], s["parent"], s["S0"],
+                                   o=s["o"], stream=stream)
+
     # fused commit-then-verify as a decoding chain: the tree recorded on
     # fctx (set i) is committed at its accepted nodes inside the verify of
     # set i + 1, the state alternating between two buffers
@@ -318,7 +324,8 @@ def main():
         # (the fused kernel serves trees of up to 128 nodes)
         if not stress_only:
             fused_reset()
-        roles = (("verify", verify), ("commit", commit)) + (() if stress_only else (("commit_verify", fused),))
+        roles = (("verify", verify), ("commit", commit)) + (
+            (("verify_static", verify_static),) if stress_only else (("commit_verify", fused),))
         for name, fn in roles:
             for i in range(args.warmup + args.steps):
                 fn(sets[i % len(sets)])
@@ -479,6 +486,10 @@ def main():
             commit(sets[i % 3])
         torch.cuda.synchronize()
         sv_ms, sc_ms = timed(verify, 30), timed(commit, 30)
+        for i in range(3):
+            verify_static(sets[i % 3])
+        torch.cuda.synchronize()
+        ss_ms = timed(verify_static, 30)
         for s in sets:
             gdn.gdn_ctx_status(s["ctx"])
         sb = verify_bytes(scfg)
@@ -487,6 +498,10 @@ def main():
                   "verify_GBps": sb / (sv_ms * 1e-3) / 1e9, "verify_frac_of_peak": sb / (sv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "verify_traffic": read_traffic("verify", STRESS),
                   "verify_kernels": "tree_kernel, then dense_kernel (two launches over the context's workspace)",
+                  "static_verify_us": ss_ms * 1e3,
+                  "static_verify_frac_of_peak": sb / (ss_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "static_verify_traffic": read_traffic("verify_static", STRESS),
+                  "static_verify_kernel": "verify_fast_kernel (gdn_tree_verify_static: no context, no workspace)",
                   "verify_nodes_heads_per_s": scfg.B * scfg.N * scfg.H_v / (sv_ms * 1e-3)}
         del ssets, sets
         torch.cuda.empty_cache()

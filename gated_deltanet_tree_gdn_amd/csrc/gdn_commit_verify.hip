@@ -21,16 +21,17 @@
 // chunk, which the persistent verify kernel's does not.  The layout:
 //   - one 32 KB buffer holds K (for the Gram and K S0^T), then Q (for
 //     Q S0^T), in the MFMA k-slot order with chunks XOR-swizzled by row;
-//   - one 40 KB area holds the tree arrays (pair lists of k.k, q.k and X,
+//   - one 40 KB area holds the tree arrays (pair lists of k.k and q.k,
 //     root paths, ancestor bits, per-node scalars) while the tree is solved,
 //     then the Z~ fragments (bf16 hi + lo, lower 16x32 blocks).
 // Rows of Z~ stay in registers between the two uses of the area.
 //
 // Phases per item: (1) parents, gates, K into LDS; (2) depth, root paths,
-// ancestor bits, the mask of 16x16 tiles holding pairs; (3) the Gram values
-// of the pairs on MFMA (wavefront w takes row tile w, Q rows from global
-// memory in the k-slot order); (4) G, gamma, X; (5) the rows of Z~ (Y formed
-// on the fly); (6) S0 and V loads, Z~ into fragments; (7) R' = V - gamma o
+// G and gamma, ancestor bits, the mask of 16x16 tiles holding pairs; (3) the
+// Gram values of the pairs on MFMA (wavefront w takes row tile w, Q rows from
+// global memory in the k-slot order); (4) each node's path into registers;
+// (5) the rows of Z~ from the Gram values, beta and the gates; (6) S0 and V
+// loads, Z~ into fragments; (7) R' = V - gamma o
 // (K S0^T) on MFMA with S0 as bf16 hi + lo; (8) Q into the buffer; (9) per
 // 16-node tile, gamma o (S0 Q^T) + R'^T Z~^T, stored as 16-byte pieces of o
 // rows (the two 16-column halves of each 128-byte piece belong to the two
@@ -52,7 +53,7 @@
 // which is the GDN delta rule applied node by node along the chunk.  One
 // wavefront that holds no tree node walks the accepted path, loads the
 // chunk's K rows, g and beta once its Gram tiles are done, and forms X and T'
-// (16 lanes, one column each, by forward substitution) in the X/Y phase;
+// (16 lanes, one column each, by forward substitution) in the path phase;
 // after the Z~ scatter every wavefront applies the chunk to its own 16 state
 // rows on MFMA (K S^T with S as bf16 hi + lo, T' and the
 // right-hand side as hi + lo, K^T from K by transposing MFMAs against the
@@ -97,14 +98,12 @@ struct ItemLds {
     // tree phase, inside the area
     static constexpr int KK = AREA;                    // float[CAP + 4]: k_i . k_s (entry CAP: sink)
     static constexpr int QK = KK + 4 * (CAP + 4);      // float[CAP + 4]: q_i . k_s
-    static constexpr int XC = QK + 4 * (CAP + 4);      // float[CAP]: X
-    static constexpr int PATH = XC + 4 * CAP;          // uint8[CAP]: the node at distance d from i
+    static constexpr int PATH = QK + 4 * (CAP + 4);    // uint8[CAP]: the node at distance d from i
     static constexpr int NODE = vi_align(PATH + CAP, 16);
     static constexpr int PAR = NODE;                   // int[NMAX]
     static constexpr int DEP = PAR + 4 * NMAX;
     static constexpr int GV = DEP + 4 * NMAX;          // float[NMAX]: g
-    static constexpr int GG = GV + 4 * NMAX;           // G
-    static constexpr int ANC = GG + 4 * NMAX;          // uint32[NMAX][AW]
+    static constexpr int ANC = GV + 4 * NMAX;          // uint32[NMAX][AW]
     static constexpr int TMASK = ANC + 4 * AW * NMAX;  // uint32[NTMAX]
     static constexpr int TREE_END = TMASK + 4 * NTMAX;
     static constexpr int AREA_BYTES = vi_align(vi_max(ZD_BYTES, TREE_END - AREA), 16);
@@ -117,7 +116,8 @@ struct ItemLds {
     static constexpr int FB_END = FB_PAR + 4 * NMAX;
     static constexpr int GAM = vi_align(vi_max(AREA + AREA_BYTES, FB_END), 16);  // float[NMAX]: gamma
     static constexpr int BET = GAM + 4 * NMAX;         // float[NMAX]: beta (kept past the tree phase)
-    static constexpr int MISC = BET + 4 * NMAX;        // int[16]
+    static constexpr int GG = BET + 4 * NMAX;          // float[NMAX]: G (kept past the tree phase)
+    static constexpr int MISC = GG + 4 * NMAX;         // int[16]
     // fused commit: one chunk of the previous tree's accepted path
     static constexpr int CK = MISC + 64;               // bf16[16][DK]: K rows (k-slot order, swizzled)
     static constexpr int CX = CK + 32 * DK;            // float[16][16]: X
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void commit_verify_kernel(Ver
     static_assert(NMAX <= NTH, "one node per thread");
     static_assert(RT * NW >= NTMAX && RT <= 2, "Gram row tiles");
     // the commit's preparing wavefront: the first one past the node threads
-    // (idle in the structure and X/Y phases, a light share of the Gram)
+    // (idle in the structure and path phases, a light share of the Gram)
     constexpr int PW = NMAX / 64;
     static_assert(PW < NW && 64 * PW >= NMAX, "the preparing wavefront holds no tree node");
 
@@ -195,7 +195,6 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void commit_verify_kernel(Ver
     unsigned char* Zd = smem + L::AREA;
     float* kk = reinterpret_cast<float*>(smem + L::KK);
     float* qk = reinterpret_cast<float*>(smem + L::QK);
-    float* xc = reinterpret_cast<float*>(smem + L::XC);
     uint8_t* pathc = smem + L::PATH;
     int* par = reinterpret_cast<int*>(smem + L::PAR);
     int* dep = reinterpret_cast<int*>(smem + L::DEP);
@@ -655,9 +654,7 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void commit_verify_kernel(Ver
     }
     __syncthreads();
 
-    // ------------------------------------------------ (4) X, Y
-    // each node's row: X_{i, t_d} = beta_i D_{i, t_d} (k_i . k_{t_d}) for the
-    // ancestor t_d at distance d >= 1, Y_{i, t_d} for d >= 0 (zero past the root)
+    // ------------------------------------------------ (4) paths
     GDN_ITEM_PHASE(3);
     // fused commit: the first chunk's T' by the preparing wavefront, which
     // holds no node
@@ -671,7 +668,6 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void commit_verify_kernel(Ver
     if (tid < NMAX) {
         const int i = tid;
         m = dep[i];
-        const float Gi = Gs[i], bi = bet[i];
 #pragma unroll
         for (int q = 0; q < ZR / 4; ++q) {
             uint32_t w = 0u;
@@ -679,42 +675,38 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void commit_verify_kernel(Ver
             for (int r = 0; r < 4; ++r) w |= static_cast<uint32_t>(pathc[i * ZR + min(4 * q + r, max(m - 1, 0))]) << (8 * r);
             ttp[q] = w;
         }
-        // X_{i, t_d} (zero at d = 0 and past the root) and, in place of
-        // q_i . k_{t_d}, Y_{i, t_d} = D_{i, t_d} (q_i . k_{t_d})
-#pragma unroll
-        for (int d = 0; d < ZR; ++d) {
-            const float D = __expf(Gi - Gs[tt(d)]);
-            xc[i * ZR + d] = d >= 1 && d < m ? bi * D * kk[i * ZR + d] : 0.f;
-            qk[i * ZR + d] = d < m ? D * qk[i * ZR + d] : 0.f;
-        }
     } else {
 #pragma unroll
         for (int q = 0; q < ZR / 4; ++q) ttp[q] = 0u;
     }
-    __syncthreads();
 
     // ------------------------------------------------ (5) rows of Z~
-    // Along the path p_0 = i, p_1, .., p_{m-1} (the root), z (I + X) = y:
-    // z_0 = y_0, and once z_d is final, z_e -= z_d X_{p_d, p_e} for e > d,
-    // where X_{p_d, p_e} sits at slot e - d of row p_d; y_d = D_{i, p_d}
-    // (q_i . k_{p_d}); the scaling z_d *= beta_{p_d} follows in (6)
+    // Along the path p_0 = i, p_1, .., p_{m-1} (the root) the row z of
+    // Y (I + X)^-1 solves z_e = Y_{i,p_e} - sum_{d < e} z_d X_{p_d,p_e}.  As
+    // D_{i,p_d} D_{p_d,p_e} = D_{i,p_e}, z_e = D_{i,p_e} y_e with
+    //     y_e = q_i . k_{p_e} - sum_{d < e} (beta_{p_d} y_d) (k_{p_d} . k_{p_e}),
+    // where k_{p_d} . k_{p_e} sits at slot e - d of row p_d.  Slots past a
+    // row's root hold no pair; what they feed is y_e for e >= m, which is
+    // dropped.  The scaling by D_{i,p_d} beta_{p_d} follows in (6).
     GDN_ITEM_PHASE(4);
     float z[ZR];
     if (tid < N) {
         const int i = tid;
 #pragma unroll
-        for (int d = 0; d < ZR; ++d) z[d] = qk[i * ZR + d];
+        for (int d = 0; d < ZR; ++d) z[d] = d < m ? qk[i * ZR + d] : 0.f;
         float xr[ZR - 1];
+        float bn = bet[tt(0)];
 #pragma unroll
-        for (int e = 0; e < ZR - 1; ++e) xr[e] = xc[tt(0) * ZR + 1 + e];
+        for (int e = 0; e < ZR - 1; ++e) xr[e] = kk[tt(0) * ZR + 1 + e];
 #pragma unroll
         for (int d = 0; d < ZR - 1; ++d) {
             float xn[ZR - 1];
 #pragma unroll
-            for (int e = 0; e + d + 2 < ZR; ++e) xn[e] = xc[tt(d + 1) * ZR + 1 + e];
-            const float zd = z[d];
+            for (int e = 0; e + d + 2 < ZR; ++e) xn[e] = kk[tt(d + 1) * ZR + 1 + e];
+            const float yd = z[d] * bn;
+            bn = bet[tt(d + 1)];
 #pragma unroll
-            for (int e = 0; e + d + 1 < ZR; ++e) z[d + 1 + e] -= zd * xr[e];
+            for (int e = 0; e + d + 1 < ZR; ++e) z[d + 1 + e] -= yd * xr[e];
 #pragma unroll
             for (int e = 0; e + d + 2 < ZR; ++e) xr[e] = xn[e];
             __builtin_amdgcn_sched_barrier(0);
@@ -758,11 +750,12 @@ __global__ __launch_bounds__(4 * DV, 4 * DV / 128) void commit_verify_kernel(Ver
         // block (I, kap) holds rows 16 I.., nodes 32 kap..; node t of row i
         // sits in lane group ((t >> 2) & 3), slot 4 ((t >> 4) & 1) + (t & 3)
         const int i = tid;
+        const float Gi = Gs[i];
 #pragma unroll
         for (int d = 0; d < ZR; ++d) {
             if (d < m) {
                 const int t = tt(d);
-                const float zb = z[d] * bet[t];
+                const float zb = z[d] * bet[t] * __expf(Gi - Gs[t]);
                 const __bf16 zh = static_cast<__bf16>(zb);
                 const __bf16 zl = static_cast<__bf16>(zb - static_cast<float>(zh));
                 const int el = (((((t >> 2) & 3) << 4) | (i & 15)) << 3) + (((t >> 4) & 1) << 2) + (t & 3);

@@ -33,7 +33,7 @@
 // (2) for a new sequence: depth and root paths (pointer jumping, prefix
 // sum), ancestor bits; (3) for a new key head, K into LDS; the Gram values
 // of the ancestor pairs (MFMA over the lower 16x16 tiles holding pairs, Q
-// rows read per row tile); (4) G, gamma, X, Y, the rows of Z~ (one thread
+// rows read per row tile); (4) G, gamma, the rows of Z~ (one thread
 // per node, in registers for paths of up to 24 nodes); (5) per wavefront:
 // K S0^T -> R', then per 16-row tile, with that tile's Q rows and Z~ blocks
 // staged in LDS by the workgroup, the transposed tile S0 Q^T + R'^T Z~^T, so
@@ -65,7 +65,9 @@ __device__ __forceinline__ uint4 mask4(uint4 v, uint32_t m) { return make_uint4(
 
 // LDS layout (bytes) for trees of at most NMAX = 256 nodes: K staged; Q read
 // from global memory per row tile (Gram) and staged per output tile; the
-// Gram values of the pairs computed per value head in place of X and Y.
+// Gram values of the pairs computed per value head (the rows of Z~ replace
+// the q_i . k_s values in place, and the Z~ blocks of an output tile reuse
+// the k_i . k_s area).
 template <int NMAX, int DK>
 struct Lds {
     static_assert(NMAX == 256, "trees of 129 to 256 nodes");
@@ -74,8 +76,11 @@ struct Lds {
     static constexpr int AW = NMAX / 32;        // ancestor bit-row words
     static constexpr int KROW = DK * 2 + 16;    // staged k / q row, padded against bank conflicts
     static constexpr int KS_OFF = 0;
-    static constexpr int XC = NMAX * KROW;      // float[CAP]: k_i . k_s, then X (per value head)
-    static constexpr int YC = XC + 4 * (CAP + 32);  // float[CAP]: q_i . k_s, then Y, then the rows of Z~ (X has 32 zero pads)
+    // float[CAP + 32]: k_i . k_s per value head; entries KZERO .. KZERO + 31
+    // are zero (the row the solve reads for path positions past a node's depth)
+    static constexpr int XC = NMAX * KROW;
+    static constexpr int KZERO = CAP;
+    static constexpr int YC = XC + 4 * (CAP + 32);  // float[CAP]: q_i . k_s, then the rows of Z~
     static constexpr int PATH = YC + 4 * CAP;   // uint8[CAP]: root..i path of every node
     static constexpr int PNODE = PATH + CAP;    // uint8[CAP]: node owning each pair
     static constexpr int NODE = (PNODE + CAP + 15) & ~15;
@@ -145,10 +150,8 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
     uint32_t* anc = reinterpret_cast<uint32_t*>(smem + L::ANC);
     uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + L::TMASK);
     int* misc = reinterpret_cast<int*>(smem + L::MISC);
-    float* xc = reinterpret_cast<float*>(smem + L::XC);
-    float* yc = reinterpret_cast<float*>(smem + L::YC);
-    float* kk = xc;   // the Gram values, turned into X and Y in place
-    float* qk = yc;
+    float* kk = reinterpret_cast<float*>(smem + L::XC);
+    float* qk = reinterpret_cast<float*>(smem + L::YC);   // q_i . k_s, then the rows of Z~ in place
     uint8_t* pathc = smem + L::PATH;
     uint8_t* pnode = smem + L::PNODE;
     unsigned char* Ks = smem + L::KS_OFF;
@@ -437,10 +440,13 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
         }
 
         GDN_PHASE(2);
-        // ---- (4) G (path sum of g) and gamma per node; X and Y per pair;
-        // per node its row of Z~ by a right-looking sweep along its path (in
-        // registers for paths of up to ZR nodes), scaled by beta of the
-        // column's node and scattered into the A-fragment blocks
+        // ---- (4) G (path sum of g) and gamma per node; per node its row of
+        // Z~ by a right-looking sweep along its path (in registers for paths
+        // of up to ZR nodes).  Along the root path t_0 .. t_{m-1} = i the row
+        // of Y (I + X)^-1 is D_{i,t_b} y_b with
+        //     y_b = q_i . k_{t_b} - sum_{a > b} (beta_{t_a} y_a) (k_{t_a} . k_{t_b})
+        // (D_{i,t_a} D_{t_a,t_b} = D_{i,t_b}), so the sweep reads the Gram
+        // values and beta only; Z~_{i,t_b} = beta_{t_b} D_{i,t_b} y_b.
         for (int i = tid; i < NMAX; i += NTH) {
             float G = 0.f;
             if (i < N) {
@@ -458,61 +464,57 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
             Gs[i] = G;
             gam[i] = i < N ? __expf(G) : 0.f;
         }
-        __syncthreads();
-        for (int p = tid; p < total; p += NTH) {
-            const int i = pnode[p], s = pathc[p];
-            const float D = __expf(Gs[i] - Gs[s]);
-            const float x = bet[i] * D * kk[p];
-            const float y = D * qk[p];
-            xc[p] = x;
-            yc[p] = y;
-        }
-        if (tid < 32) xc[total + tid] = 0.f;  // pads read by the branch-free solve below
+        // the zero row read for path positions past a node's depth (a walked
+        // item may have overwritten it)
+        if (tid < 32) kk[L::KZERO + tid] = 0.f;
         __syncthreads();
         for (int i = tid; i < N; i += NTH) {
             const int o = off[i], m = dep[i];
+            const float Gi = Gs[i];
             if (m <= ZR) {
-                // branch-free: entries past the path are zero and their X
-                // reads land on finite values (pairs of later nodes or the
-                // zero pads), so loads can be issued early
-                int t[ZR], oa[ZR];
-                float z[ZR];
+                // branch-free: positions past the path read the zero row, so
+                // loads can be issued early
+                int oa[ZR];
+                float y[ZR], bt[ZR];
 #pragma unroll
                 for (int bb = 0; bb < ZR; ++bb) {
                     const int pp = o + min(bb, m - 1);
-                    t[bb] = pathc[pp];
-                    oa[bb] = off[t[bb]];
-                    z[bb] = bb < m ? yc[pp] : 0.f;
+                    const int t = pathc[pp];
+                    oa[bb] = bb < m ? off[t] : L::KZERO;
+                    bt[bb] = bet[t];
+                    y[bb] = bb < m ? qk[pp] : 0.f;
                 }
-                // one row of X in flight ahead of the row being applied
+                // one row of k.k in flight ahead of the row being applied
                 float xr[ZR - 1];
 #pragma unroll
-                for (int bb = 0; bb < ZR - 1; ++bb) xr[bb] = xc[oa[ZR - 1] + bb];
+                for (int bb = 0; bb < ZR - 1; ++bb) xr[bb] = kk[oa[ZR - 1] + bb];
 #pragma unroll
                 for (int aa = ZR - 1; aa >= 1; --aa) {
                     float xn[ZR - 1];
 #pragma unroll
-                    for (int bb = 0; bb + 1 < aa; ++bb) xn[bb] = xc[oa[aa - 1] + bb];
-                    const float za = z[aa];
+                    for (int bb = 0; bb + 1 < aa; ++bb) xn[bb] = kk[oa[aa - 1] + bb];
+                    const float ya = y[aa] * bt[aa];
 #pragma unroll
-                    for (int bb = 0; bb < aa; ++bb) z[bb] -= za * xr[bb];
+                    for (int bb = 0; bb < aa; ++bb) y[bb] -= ya * xr[bb];
 #pragma unroll
                     for (int bb = 0; bb + 1 < aa; ++bb) xr[bb] = xn[bb];
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
-                for (int bb = 0; bb < ZR; ++bb) z[bb] *= bet[t[bb]];
-#pragma unroll
                 for (int bb = 0; bb < ZR; ++bb)
-                    if (bb < m) yc[o + bb] = z[bb];
+                    if (bb < m) qk[o + bb] = y[bb] * bt[bb] * __expf(Gi - Gs[pathc[o + bb]]);
                 continue;
             }
             for (int aa = m - 1; aa >= 1; --aa) {
-                const float za = yc[o + aa];
-                const int oa = off[pathc[o + aa]];
-                for (int bb = 0; bb < aa; ++bb) yc[o + bb] -= za * xc[oa + bb];
+                const int ta = pathc[o + aa];
+                const float ya = qk[o + aa] * bet[ta];
+                const int oa = off[ta];
+                for (int bb = 0; bb < aa; ++bb) qk[o + bb] -= ya * kk[oa + bb];
             }
-            for (int bb = 0; bb < m; ++bb) yc[o + bb] *= bet[pathc[o + bb]];
+            for (int bb = 0; bb < m; ++bb) {
+                const int t = pathc[o + bb];
+                qk[o + bb] *= bet[t] * __expf(Gi - Gs[t]);
+            }
         }
         __syncthreads();
         GDN_PHASE(3);
@@ -613,7 +615,7 @@ __global__ __launch_bounds__(64 * NW) void verify_fast_kernel(VerifyArgs a, int 
                 const int p1 = 16 * I + 16 < N ? off[16 * I + 16] : total;
                 for (int p = p0 + tid; p < p1; p += NTH) {
                     const int i = pnode[p], tt = pathc[p];
-                    const float zz = yc[p];
+                    const float zz = qk[p];
                     const __bf16 zh = static_cast<__bf16>(zz);
                     const __bf16 zl = static_cast<__bf16>(zz - static_cast<float>(zh));
                     const int e = (((((tt >> 2) & 3) << 4) | (i & 15)) << 3) + (((tt >> 4) & 1) << 2) + (tt & 3);
