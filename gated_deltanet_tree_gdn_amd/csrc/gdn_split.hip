@@ -21,10 +21,12 @@
 // the ancestor pairs, the row solve) is a long chain of dependent
 // phases, and an item's dense side needs most of a compute unit's LDS and
 // registers, so the two cannot share a workgroup without running in turn.
-// Here the tree kernel runs the chains of the whole batch side by side, one
-// workgroup per (sequence, key head) that computes the Gram once for the
-// value heads of the key head and solves two value heads at a time, and the
-// dense kernel runs one item per workgroup, two workgroups per compute unit.
+// Here the tree kernel runs the chains of the whole batch side by side: one
+// persistent workgroup per compute unit walks a run of (sequence, key head)
+// items, builds a sequence's structure once for its run, computes the Gram
+// once for the value heads of each key head, solves two value heads at a
+// time, and loads the next item's rows while it solves; the dense kernel
+// runs one item per workgroup, two workgroups per compute unit.
 // Between them go the pair values (4 bytes per ancestor pair and value
 // head) and gamma; K and Q are read by both.  (For trees of at most 128
 // nodes the persistent single-launch kernel of gdn_verify_ws.hip, which
@@ -97,11 +99,15 @@ struct TreeLds {
     static constexpr int TOTAL = MISC + 64;
 };
 
-// One workgroup per (sequence, key head), 2 NMAX threads: the structure and
-// the Gram of the key head once, then the value heads of the key head two at
-// a time, thread t taking node t mod NMAX of head slot t / NMAX.
+// A persistent grid: one workgroup per compute unit, 2 NMAX threads, walking
+// a run of consecutive (sequence, key head) items.  Per item the Gram of the
+// key head once, then the value heads of the key head two at a time, thread t
+// taking node t mod NMAX of head slot t / NMAX.  Items of one sequence share
+// its structure (depth, pair offsets, root paths, the tiles holding pairs),
+// built for the first of them; the next item's parents, gates of its first
+// two value heads and Q/K rows are loaded while the current item is solved.
 template <int NMAX, int DK>
-__global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w) {
+__global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w, int items_per_wg) {
     using L = TreeLds<NMAX, DK>;
     constexpr int NTH = 2 * NMAX;
     constexpr int NW = NTH / 64;
@@ -115,15 +121,33 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
 
     __shared__ __align__(16) unsigned char smem[L::TOTAL];
     GDN_SPLIT_PHASE_DECL
-    GDN_SPLIT_PHASE(0);
 
     const int N = a.N, Hk = a.H_k, Hv = a.H_v;
     const int R = Hv / Hk;
-    const int b = blockIdx.x / Hk, kh = blockIdx.x % Hk;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, lc = lane & 15, lg = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ni = tid % NMAX, hr = tid / NMAX;
+    const int n_items = a.B * Hk;
+    // Workgroups go to the 8 XCDs in turn; numbering them so that each XCD
+    // takes consecutive items keeps the key heads of a sequence on one XCD,
+    // whose L2 then serves their shared rows of g, beta and the parents once
+    const int wg = gridDim.x % 8 == 0 ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int it0 = wg * items_per_wg;
+    const int it1 = min(it0 + items_per_wg, n_items);
+    if (it0 >= it1) return;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    // The thread index is refreshed through an opaque copy once per item:
+    // addresses derived from it are then recomputed per item rather than
+    // hoisted out of the item loop and held in registers across it.
+    int tid, lane, lc, lg, ni, hr;
+    auto refresh = [&]() {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        tid = t;
+        lane = t & 63;
+        lc = lane & 15;
+        lg = lane >> 4;
+        ni = t % NMAX;
+        hr = t / NMAX;
+    };
+    refresh();
 
     const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(a.q);
     const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(a.k);
@@ -142,13 +166,8 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
     uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + L::TMASK);
     int* misc = reinterpret_cast<int*>(smem + L::MISC);
 
-    // ---- (1) parents, g and beta of the first two value heads (which the
-    // structure phases wait for, so they are issued first), then the Q rows
-    // of this wavefront's Gram row tiles and the K rows, held in registers
-    // through the structure phases
-    int p = -1;
-    if (tid < NMAX && tid < N) p = a.parent[static_cast<size_t>(b) * N + tid];
-    auto load_gb = [&](int r0, float& gi, float& bi) {
+    // g and beta of value head kh R + r0 + hr at node ni
+    auto load_gb = [&](int b, int kh, int r0, float& gi, float& bi) {
         const int r = r0 + hr;
         gi = 0.f;
         bi = 0.f;
@@ -162,277 +181,317 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w)
         gv[hr * NMAX + ni] = gi;
         bet[hr * NMAX + ni] = bi;
     };
-    float g0, b0;
-    load_gb(0, g0, b0);
     auto row_tile = [&](int u) { return u == 0 ? wave : 2 * NW - 1 - wave; };
-    bf16x8 qa[RU][KS];
-#pragma unroll
-    for (int u = 0; u < RU; ++u)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qa[u][ks] = load_frag(qg + ((static_cast<size_t>(b) * N + min(16 * row_tile(u) + lc, N - 1)) * Hk + kh) * DK +
-                                  8 * KS * lg + 8 * ks);
-    // K rows: loaded now, written to LDS after the structure phases, which
-    // their latency overlaps
-    uint4 kv[KCH];
-#pragma unroll
-    for (int q = 0; q < KCH; ++q) {
-        const int e = tid + q * NTH;
-        const int row = min(e / (DK / 8), N - 1);
-        kv[q] = *reinterpret_cast<const uint4*>(kg + ((static_cast<size_t>(b) * N + row) * Hk + kh) * DK + (e % (DK / 8)) * 8);
-    }
-    store_gb(g0, b0);
-    int bad_local = 0;
-    if (tid < NMAX) {
-        const int i = tid;
-        if (i < N && (p < -1 || p >= i)) {
-            bad_local = 1;
-            p = -1;
-        }
-        par[i] = p;
-        nxt[i] = p;
-        dep[i] = i < N ? 1 : 0;
-    }
-    if (tid < NTMAX) tmask[tid] = 0u;
-    if (tid >= 64 && tid < 64 + 32) kk[L::KZERO + tid - 64] = 0.f;
-    const int bad = __syncthreads_or(bad_local);
-    GDN_SPLIT_PHASE(1);
 
-    // ---- (2) structure: depth by pointer jumping (dep[i] counts the nodes
-    // from i up to nxt[i]), pair offsets, root paths, the tiles holding pairs
-    for (int round = 0; round < 9; ++round) {
-        int c2 = 0, n2 = -1;
-        if (tid < NMAX) {
-            const int nx = nxt[tid];
-            c2 = dep[tid] + (nx >= 0 ? dep[nx] : 0);
-            n2 = nx >= 0 ? nxt[nx] : -1;
+    // ---- (1) an item's loads, in flight until it starts: the parents and
+    // the gates of its first two value heads (which the structure phases wait
+    // for, so they are issued first), the Q rows of this wavefront's Gram row
+    // tiles, and the K rows (written to LDS once the previous item's Gram is
+    // done)
+    int p_pf = -1;
+    float g_pf = 0.f, b_pf = 0.f;
+    bf16x8 qa[RU][KS];
+    uint4 kv[KCH];
+    auto prefetch = [&](int it) {
+        const int b = it / Hk, kh = it % Hk;
+        p_pf = tid < NMAX && tid < N ? a.parent[static_cast<size_t>(b) * N + tid] : -1;
+        load_gb(b, kh, 0, g_pf, b_pf);
+#pragma unroll
+        for (int u = 0; u < RU; ++u)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qa[u][ks] = load_frag(qg + ((static_cast<size_t>(b) * N + min(16 * row_tile(u) + lc, N - 1)) * Hk + kh) * DK +
+                                      8 * KS * lg + 8 * ks);
+#pragma unroll
+        for (int q = 0; q < KCH; ++q) {
+            const int e = tid + q * NTH;
+            const int row = min(e / (DK / 8), N - 1);
+            kv[q] = *reinterpret_cast<const uint4*>(kg + ((static_cast<size_t>(b) * N + row) * Hk + kh) * DK + (e % (DK / 8)) * 8);
+        }
+    };
+    prefetch(it0);
+    if (tid >= 64 && tid < 64 + 32) kk[L::KZERO + tid - 64] = 0.f;
+
+    int cur_b = -1, bad = 0, deep = 0;
+    for (int it = it0; it < it1; ++it) {
+        GDN_SPLIT_PHASE(0);
+        refresh();
+        const int b = it / Hk, kh = it % Hk;
+        const bool new_b = b != cur_b;
+        cur_b = b;
+        store_gb(g_pf, b_pf);
+        int bad_local = 0;
+        if (new_b) {
+            if (tid < NMAX) {
+                const int i = tid;
+                int p = p_pf;
+                if (i < N && (p < -1 || p >= i)) {
+                    bad_local = 1;
+                    p = -1;
+                }
+                par[i] = p;
+                nxt[i] = p;
+                dep[i] = i < N ? 1 : 0;
+            }
+            if (tid < NTMAX) tmask[tid] = 0u;
+        }
+        {
+            const int any_bad = __syncthreads_or(bad_local);
+            if (new_b) bad = any_bad;
+        }
+        GDN_SPLIT_PHASE(1);
+
+        // ---- (2) for a new sequence, the structure: depth by pointer
+        // jumping (dep[i] counts the nodes from i up to nxt[i]), pair
+        // offsets, root paths, the tiles holding pairs
+        if (new_b) {
+            for (int round = 0; round < 9; ++round) {
+                int c2 = 0, n2 = -1;
+                if (tid < NMAX) {
+                    const int nx = nxt[tid];
+                    c2 = dep[tid] + (nx >= 0 ? dep[nx] : 0);
+                    n2 = nx >= 0 ? nxt[nx] : -1;
+                }
+                __syncthreads();
+                if (tid < NMAX) {
+                    dep[tid] = c2;
+                    nxt[tid] = n2;
+                }
+                if (!__syncthreads_or(n2 >= 0)) break;
+            }
+            deep = __syncthreads_or(tid < N && dep[tid] > ZR);
+        }
+        GDN_SPLIT_PHASE(2);
+        if (kh == 0 && tid == 0) {
+            a.tree_status[b] = bad ? GDN_ERR_TREE : 0;
+            w.deep[b] = deep ? 1 : 0;
+        }
+        if (deep) {
+            // the dense kernel walks this sequence
+            if (it + 1 < it1) prefetch(it + 1);
+            continue;
+        }
+        if (new_b && wave == 0) {
+            // exclusive scan of dep into off; off[N] = pair count
+            constexpr int E = NMAX / 64;
+            int vals[E];
+            int sum = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                vals[e] = dep[lane * E + e];
+                sum += vals[e];
+            }
+            int incl = sum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += t;
+            }
+            int run = incl - sum;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                off[lane * E + e] = run;
+                run += vals[e];
+            }
+            if (lane == 63) {
+                off[NMAX] = incl;
+                misc[0] = incl;
+            }
         }
         __syncthreads();
-        if (tid < NMAX) {
-            dep[tid] = c2;
-            nxt[tid] = n2;
+        const int total = misc[0];
+#pragma unroll
+        for (int q = 0; q < KCH; ++q) {
+            const int e = tid + q * NTH;
+            const int row = e / (DK / 8), cc = e % (DK / 8);
+            const uint4 v = row < N ? kv[q] : make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint4*>(Ks + row * L::KROW + cc * 16) = v;
         }
-        if (!__syncthreads_or(n2 >= 0)) break;
-    }
-    const int deep = __syncthreads_or(tid < N && dep[tid] > ZR);
-    GDN_SPLIT_PHASE(2);
-    if (kh == 0 && tid == 0) {
-        a.tree_status[b] = bad ? GDN_ERR_TREE : 0;
-        w.deep[b] = deep ? 1 : 0;
-    }
-    if (deep) return;
-    if (wave == 0) {
-        // exclusive scan of dep into off; off[N] = pair count
-        constexpr int E = NMAX / 64;
-        int vals[E];
-        int sum = 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            vals[e] = dep[lane * E + e];
-            sum += vals[e];
-        }
-        int incl = sum;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int t = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += t;
-        }
-        int run = incl - sum;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            off[lane * E + e] = run;
-            run += vals[e];
-        }
-        if (lane == 63) {
-            off[NMAX] = incl;
-            misc[0] = incl;
-        }
-    }
-    __syncthreads();
-    const int total = misc[0];
-#pragma unroll
-    for (int q = 0; q < KCH; ++q) {
-        const int e = tid + q * NTH;
-        const int row = e / (DK / 8), cc = e % (DK / 8);
-        const uint4 v = row < N ? kv[q] : make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(Ks + row * L::KROW + cc * 16) = v;
-    }
-    if (tid < NMAX && tid < N) {
-        // node i's root path, root first, at its pairs; the tiles that hold
-        // pairs; (key head 0) where each pair's entry goes in the dense
-        // kernel's blocks: block s / 32 (2 KB: 1 KB hi, then 1 KB lo) of the
-        // row tile, lane group (s / 4) mod 4, row i mod 16, slot
-        // 4 ((s / 16) mod 2) + s mod 4 of that lane's 8 bf16
-        const int i = tid;
-        uint16_t* zg = w.zoff + static_cast<size_t>(b) * w.P;
-        int pos = off[i] + dep[i] - 1;
-        uint32_t mask = 0u;
-        for (int s = i; s >= 0; s = par[s]) {
-            pathc[pos] = static_cast<uint8_t>(s);
-            if (kh == 0) {
-                const int el = (((((s >> 2) & 3) << 4) | (i & 15)) << 3) + (((s >> 4) & 1) << 2) + (s & 3);
-                zg[pos] = static_cast<uint16_t>(2048 * (s >> 5) + 2 * el);
-            }
-            --pos;
-            mask |= 1u << (s >> 4);
-        }
-        atomicOr(&tmask[i >> 4], mask);
-    }
-    __syncthreads();
-    GDN_SPLIT_PHASE(3);
-    if (kh == 0) {
-        // the rest of the sequence's pair structure for the dense kernel
-        int32_t* offg = w.off + static_cast<size_t>(b) * (N + 1);
-        for (int i = tid; i <= N; i += NTH) offg[i] = i < N ? off[i] : total;
-    }
-
-    // ---- (3) Gram values of the ancestor pairs: MFMA over the lower 16x16
-    // tiles that hold pairs; wavefront w takes row tiles w and 2 NW - 1 - w
-    // (their Q rows were loaded on entry)
-    {
-        const int NT = (N + 15) >> 4;
-        auto k_frag = [&](int row, int ks) -> bf16x8 {
-            return load_frag(Ks + row * L::KROW + 2 * (8 * KS * lg + 8 * ks));
-        };
-#pragma unroll
-        for (int u = 0; u < RU; ++u) {
-            const int I = row_tile(u);
-            if (I >= NT) continue;
-            const uint32_t tm = tmask[I];
-            bf16x8 ka[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) ka[ks] = k_frag(16 * I + lc, ks);
-            // this lane's rows i = 16 I + 4 lg + rr: first pair and depth
-            int oi[4], di[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int i = 16 * I + 4 * lg + rr;
-                oi[rr] = off[i];
-                di[rr] = i < N ? dep[i] : 0;
-            }
-            // tiles J <= I that hold pairs, in order; the K fragments of tile
-            // J, the depth of its node s = 16 J + lc and the root-path bytes
-            // at which the lane's four pairs (i, s) would sit are read one
-            // tile ahead
-            const uint32_t todo = tm & ((2u << I) - 1u);
-            struct Ahead {
-                bf16x8 kb[KS];
-                int ds;
-                int pc[4];
-            };
-            auto read_ahead = [&](int J) __attribute__((always_inline)) {
-                Ahead r;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) r.kb[ks] = k_frag(16 * J + lc, ks);
-                r.ds = dep[16 * J + lc];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) r.pc[rr] = pathc[min(max(oi[rr] + r.ds - 1, 0), L::CAP - 1)];
-                return r;
-            };
-            uint32_t left = todo;
-            if (!left) continue;
-            int J = __builtin_ctz(left);
-            left &= left - 1;
-            Ahead cur = read_ahead(J);
-            for (;;) {
-                f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    akk = mfma(ka[ks], cur.kb[ks], akk);
-                    aqk = mfma(qa[u][ks], cur.kb[ks], aqk);
+        if (new_b && tid < NMAX && tid < N) {
+            // node i's root path, root first, at its pairs; the tiles that
+            // hold pairs; (key head 0) where each pair's entry goes in the
+            // dense kernel's blocks: block s / 32 (2 KB: 1 KB hi, then 1 KB
+            // lo) of the row tile, lane group (s / 4) mod 4, row i mod 16,
+            // slot 4 ((s / 16) mod 2) + s mod 4 of that lane's 8 bf16.  Key
+            // head 0 is always the first item of its sequence in a run.
+            const int i = tid;
+            uint16_t* zg = w.zoff + static_cast<size_t>(b) * w.P;
+            int pos = off[i] + dep[i] - 1;
+            uint32_t mask = 0u;
+            for (int s = i; s >= 0; s = par[s]) {
+                pathc[pos] = static_cast<uint8_t>(s);
+                if (kh == 0) {
+                    const int el = (((((s >> 2) & 3) << 4) | (i & 15)) << 3) + (((s >> 4) & 1) << 2) + (s & 3);
+                    zg[pos] = static_cast<uint16_t>(2048 * (s >> 5) + 2 * el);
                 }
-                const int Jn = left ? __builtin_ctz(left) : -1;
-                left &= left - 1;
-                Ahead nxt;
-                if (Jn >= 0) nxt = read_ahead(Jn);
-                // lane: rows i = 16 I + 4 lg + rr, column node s = 16 J + lc;
-                // s is an ancestor of i (or i) exactly when i's root path
-                // holds s at position dep[s] - 1, where the pair is stored
-                const int sn = 16 * J + lc;
+                --pos;
+                mask |= 1u << (s >> 4);
+            }
+            atomicOr(&tmask[i >> 4], mask);
+        }
+        __syncthreads();
+        GDN_SPLIT_PHASE(3);
+        if (kh == 0) {
+            // the rest of the sequence's pair structure for the dense kernel
+            int32_t* offg = w.off + static_cast<size_t>(b) * (N + 1);
+            for (int i = tid; i <= N; i += NTH) offg[i] = i < N ? off[i] : total;
+        }
+
+        // ---- (3) Gram values of the ancestor pairs: MFMA over the lower
+        // 16x16 tiles that hold pairs; wavefront w takes row tiles w and
+        // 2 NW - 1 - w (their Q rows came with the item's loads)
+        {
+            const int NT = (N + 15) >> 4;
+            auto k_frag = [&](int row, int ks) -> bf16x8 {
+                return load_frag(Ks + row * L::KROW + 2 * (8 * KS * lg + 8 * ks));
+            };
+#pragma unroll
+            for (int u = 0; u < RU; ++u) {
+                const int I = row_tile(u);
+                if (I >= NT) continue;
+                const uint32_t tm = tmask[I];
+                bf16x8 ka[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) ka[ks] = k_frag(16 * I + lc, ks);
+                // this lane's rows i = 16 I + 4 lg + rr: first pair and depth
+                int oi[4], di[4];
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
-                    if (cur.ds >= 1 && cur.ds <= di[rr] && cur.pc[rr] == sn) {
-                        const int pp = oi[rr] + cur.ds - 1;
-                        kk[pp] = akk[rr];
-                        qk[pp] = aqk[rr];
-                    }
+                    const int i = 16 * I + 4 * lg + rr;
+                    oi[rr] = off[i];
+                    di[rr] = i < N ? dep[i] : 0;
                 }
-                if (Jn < 0) break;
-                J = Jn;
-                cur = nxt;
+                // tiles J <= I that hold pairs, in order; the K fragments of
+                // tile J, the depth of its node s = 16 J + lc and the
+                // root-path bytes at which the lane's four pairs (i, s) would
+                // sit are read one tile ahead
+                const uint32_t todo = tm & ((2u << I) - 1u);
+                struct Ahead {
+                    bf16x8 kb[KS];
+                    int ds;
+                    int pc[4];
+                };
+                auto read_ahead = [&](int J) __attribute__((always_inline)) {
+                    Ahead r;
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) r.kb[ks] = k_frag(16 * J + lc, ks);
+                    r.ds = dep[16 * J + lc];
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) r.pc[rr] = pathc[min(max(oi[rr] + r.ds - 1, 0), L::CAP - 1)];
+                    return r;
+                };
+                uint32_t left = todo;
+                if (!left) continue;
+                int J = __builtin_ctz(left);
+                left &= left - 1;
+                Ahead cur = read_ahead(J);
+                for (;;) {
+                    f32x4 akk = {0.f, 0.f, 0.f, 0.f}, aqk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        akk = mfma(ka[ks], cur.kb[ks], akk);
+                        aqk = mfma(qa[u][ks], cur.kb[ks], aqk);
+                    }
+                    const int Jn = left ? __builtin_ctz(left) : -1;
+                    left &= left - 1;
+                    Ahead nx;
+                    if (Jn >= 0) nx = read_ahead(Jn);
+                    // lane: rows i = 16 I + 4 lg + rr, column node s = 16 J +
+                    // lc; s is an ancestor of i (or i) exactly when i's root
+                    // path holds s at position dep[s] - 1, where the pair is
+                    // stored
+                    const int sn = 16 * J + lc;
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        if (cur.ds >= 1 && cur.ds <= di[rr] && cur.pc[rr] == sn) {
+                            const int pp = oi[rr] + cur.ds - 1;
+                            kk[pp] = akk[rr];
+                            qk[pp] = aqk[rr];
+                        }
+                    }
+                    if (Jn < 0) break;
+                    J = Jn;
+                    cur = nx;
+                }
             }
         }
-    }
-    __syncthreads();
-    GDN_SPLIT_PHASE(4);
-
-    // ---- (4) per pair of value heads: G, gamma; rows of Z~.  Along node i's
-    // root path t_0 (root) .. t_{m-1} = i the row w of Y (I + X)^-1 solves
-    // w_b = Y_{i,t_b} - sum_{a > b} w_a X_{t_a,t_b}.  As D_{i,t_a} D_{t_a,t_b} =
-    // D_{i,t_b}, w_b = D_{i,t_b} y_b with
-    //     y_b = q_i . k_{t_b} - sum_{a > b} (beta_{t_a} y_a) (k_{t_a} . k_{t_b}),
-    // a sweep over the Gram values and beta only; Z~_{i,t_b} = beta_{t_b} w_b.
-    for (int r0 = 0; r0 < R; r0 += 2) {
-        if (r0 > 0) {
-            __syncthreads();   // the previous pair's reads of gv, bet and Gs are done
-            float gi, bi;
-            load_gb(r0, gi, bi);
-            store_gb(gi, bi);
-            __syncthreads();
-        }
-        const int r = r0 + hr;
-        const bool live = r < R && ni < N;
-        const int h = kh * R + r;
-        const int o = off[ni], m = live ? dep[ni] : 0;
-        const float* gvh = gv + hr * NMAX;
-        const float* bh = bet + hr * NMAX;
-        float* Gh = Gs + hr * NMAX;
-        auto path_at = [&](int d) {
-            return min(static_cast<int>(pathc[min(o + min(d, max(m - 1, 0)), L::CAP - 1)]), NMAX - 1);
-        };
-        float G = 0.f;
-#pragma unroll
-        for (int d = 0; d < ZR; ++d) G += d < m ? gvh[path_at(d)] : 0.f;
-        Gh[ni] = G;
-        if (live) w.gam[(static_cast<size_t>(b) * Hv + h) * N + ni] = __expf(G);
+        // the next item's loads, in flight through the solve below
+        if (it + 1 < it1) prefetch(it + 1);
         __syncthreads();
-        GDN_SPLIT_PHASE(5);
-        GDN_SPLIT_PHASE(6);
-        if (live) {
-            // swept from the node end: once y_a is final, y_b -= beta_{t_a} y_a
-            // (k_{t_a} . k_{t_b}) for b < a, the Gram value at position b of
-            // t_a's root path; positions past the path read the zero row
-            int oa[ZR];
-            float y[ZR], bt[ZR];
-#pragma unroll
-            for (int d = 0; d < ZR; ++d) {
-                const int t = path_at(d);
-                oa[d] = d < m ? off[t] : L::KZERO;
-                bt[d] = bh[t];
-                y[d] = d < m ? qk[o + d] : 0.f;
+        GDN_SPLIT_PHASE(4);
+
+        // ---- (4) per pair of value heads: G, gamma; rows of Z~.  Along node
+        // i's root path t_0 (root) .. t_{m-1} = i the row w of Y (I + X)^-1
+        // solves w_b = Y_{i,t_b} - sum_{a > b} w_a X_{t_a,t_b}.  As
+        // D_{i,t_a} D_{t_a,t_b} = D_{i,t_b}, w_b = D_{i,t_b} y_b with
+        //     y_b = q_i . k_{t_b} - sum_{a > b} (beta_{t_a} y_a) (k_{t_a} . k_{t_b}),
+        // a sweep over the Gram values and beta only; Z~_{i,t_b} = beta_{t_b} w_b.
+        for (int r0 = 0; r0 < R; r0 += 2) {
+            if (r0 > 0) {
+                __syncthreads();   // the previous pair's reads of gv, bet and Gs are done
+                float gi, bi;
+                load_gb(b, kh, r0, gi, bi);
+                store_gb(gi, bi);
+                __syncthreads();
             }
-            float xr[ZR - 1];
+            const int r = r0 + hr;
+            const bool live = r < R && ni < N;
+            const int h = kh * R + r;
+            const int o = off[ni], m = live ? dep[ni] : 0;
+            const float* gvh = gv + hr * NMAX;
+            const float* bh = bet + hr * NMAX;
+            float* Gh = Gs + hr * NMAX;
+            auto path_at = [&](int d) {
+                return min(static_cast<int>(pathc[min(o + min(d, max(m - 1, 0)), L::CAP - 1)]), NMAX - 1);
+            };
+            float G = 0.f;
 #pragma unroll
-            for (int e = 0; e < ZR - 1; ++e) xr[e] = kk[oa[ZR - 1] + e];
+            for (int d = 0; d < ZR; ++d) G += d < m ? gvh[path_at(d)] : 0.f;
+            Gh[ni] = G;
+            if (live) w.gam[(static_cast<size_t>(b) * Hv + h) * N + ni] = __expf(G);
+            __syncthreads();
+            GDN_SPLIT_PHASE(5);
+            GDN_SPLIT_PHASE(6);
+            if (live) {
+                // swept from the node end: once y_a is final, y_b -=
+                // beta_{t_a} y_a (k_{t_a} . k_{t_b}) for b < a, the Gram value
+                // at position b of t_a's root path; positions past the path
+                // read the zero row
+                int oa[ZR];
+                float y[ZR], bt[ZR];
 #pragma unroll
-            for (int aa = ZR - 1; aa >= 1; --aa) {
-                float xn[ZR - 1];
+                for (int d = 0; d < ZR; ++d) {
+                    const int t = path_at(d);
+                    oa[d] = d < m ? off[t] : L::KZERO;
+                    bt[d] = bh[t];
+                    y[d] = d < m ? qk[o + d] : 0.f;
+                }
+                float xr[ZR - 1];
 #pragma unroll
-                for (int e = 0; e + 1 < aa; ++e) xn[e] = kk[oa[aa - 1] + e];
-                const float ya = y[aa] * bt[aa];
+                for (int e = 0; e < ZR - 1; ++e) xr[e] = kk[oa[ZR - 1] + e];
 #pragma unroll
-                for (int e = 0; e < aa; ++e) y[e] -= ya * xr[e];
+                for (int aa = ZR - 1; aa >= 1; --aa) {
+                    float xn[ZR - 1];
 #pragma unroll
-                for (int e = 0; e + 1 < aa; ++e) xr[e] = xn[e];
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int e = 0; e + 1 < aa; ++e) xn[e] = kk[oa[aa - 1] + e];
+                    const float ya = y[aa] * bt[aa];
+#pragma unroll
+                    for (int e = 0; e < aa; ++e) y[e] -= ya * xr[e];
+#pragma unroll
+                    for (int e = 0; e + 1 < aa; ++e) xr[e] = xn[e];
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                float* zg = w.z + (static_cast<size_t>(b) * Hv + h) * w.P + o;
+#pragma unroll
+                for (int d = 0; d < ZR; ++d)
+                    if (d < m) zg[d] = y[d] * bt[d] * __expf(G - Gh[path_at(d)]);
             }
-            float* zg = w.z + (static_cast<size_t>(b) * Hv + h) * w.P + o;
-#pragma unroll
-            for (int d = 0; d < ZR; ++d)
-                if (d < m) zg[d] = y[d] * bt[d] * __expf(G - Gh[path_at(d)]);
         }
+        // every read of this item's LDS arrays is done before the next item
+        // writes them
+        __syncthreads();
+        GDN_SPLIT_PHASE(7);
     }
-    GDN_SPLIT_PHASE(7);
     GDN_SPLIT_PHASE_END(0, blockIdx.x);
 }
 
@@ -794,7 +853,12 @@ __global__ __launch_bounds__(4 * DV / CT, 2) void dense_kernel(VerifyArgs a, Spl
 
 template <int NMAX, int DK, int DV>
 hipError_t launch_split_t(const VerifyArgs& a, const SplitWs& w, hipStream_t stream) {
-    hipLaunchKernelGGL((tree_kernel<NMAX, DK>), dim3(static_cast<unsigned>(a.B) * a.H_k), dim3(2 * NMAX), 0, stream, a, w);
+    // one tree workgroup per compute unit, each taking a run of
+    // (sequence, key head) items
+    const int items = a.B * a.H_k;
+    const int wgs = min(items, device_cus());
+    const int per = (items + wgs - 1) / wgs;
+    hipLaunchKernelGGL((tree_kernel<NMAX, DK>), dim3((items + per - 1) / per), dim3(2 * NMAX), 0, stream, a, w, per);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // two column tiles per wavefront at d_v = 128 (4 wavefronts), one at 64
