@@ -42,6 +42,12 @@
  *    whose tree or accepted node is invalid are unspecified (but every
  *    access stays in bounds).
  *  - Non-finite inputs propagate; they are not checked.
+ *  - Range: results are stated for beta in [0, 1] and |k_i|^2 <= 2 (Gated
+ *    DeltaNet normalises k to unit length and takes beta in (0, 1)).  There
+ *    beta_a |k_a . k_b| <= 2, so the fp32 intermediates of the tree solve
+ *    grow by at most 3x per root-path node and stay finite.  Outside it they
+ *    can overflow on long root paths even where strong decay keeps the true
+ *    result finite.
  *  - GDN_FORCE_SIMPLE=1 (read when a context is created) routes that
  *    context's verify to the per-node walk kernels instead of the MFMA path
  *    (for A/B comparison; results agree within the stated tolerance).

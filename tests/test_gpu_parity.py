@@ -542,6 +542,60 @@ def test_pair_list_capacity_boundary(N, spines, expect):
     assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), "capacity boundary o")
 
 
+def _edge_of_stable_inputs(N, depth, seed):
+    """keys at |k|^2 = 2 and beta = 1 (the edge of the stated input range,
+    beta in [0, 1] and |k|^2 <= 2), gates -8 along a spine of `depth` nodes
+    in sequence 0 (the spine shares one key, so k.k = 2 on every spine pair,
+    and the decay across it underflows in fp32), a best-first tree of depth
+    <= `depth` in sequence 1"""
+    cfg = G.shrink(G.CONFIGS["bestfirst128"], B=2, H_k=2, H_v=4, N=N, max_depth=depth)
+    inp = G.make_inputs(cfg, seed=seed)
+    rng = np.random.default_rng(seed)
+    par = inp["parent"].copy()
+    par[0, 0] = -1
+    par[0, 1:depth] = np.arange(depth - 1)
+    par[0, depth:] = rng.integers(0, depth // 2, size=N - depth)
+    inp["parent"] = par
+    k = inp["k"] * np.float32(np.sqrt(2.0))
+    k[0, :depth] = k[0, :1]
+    inp["k_bits"] = G.round_bf16_bits(k)
+    inp["k"] = G.bf16_bits_to_f32(inp["k_bits"])
+    inp["beta"][:] = 1.0
+    inp["g"][0, :depth] = -8.0
+    return cfg, inp
+
+
+@pytest.mark.parametrize("N,depth", [(128, 16), (256, 24)])
+def test_solve_at_edge_of_stable_range(N, depth):
+    """the row solve of Z~ runs on the Gram values and beta and applies the
+    decay afterwards; its intermediates grow by at most 1 + 2 = 3x per path
+    node when beta |k_a . k_b| <= 2, finite in fp32 over root paths of 16 and
+    24 nodes.  Context verify, commit, the allocation-free verify and
+    (N = 128) the fused commit-then-verify, against the oracle"""
+    cfg, inp = _edge_of_stable_inputs(N, depth, seed=31)
+    d = G.to_device(inp)
+    say(f"[edge of stable range] N={N} depth={depth}")
+    o, ctx = run_verify(d)
+    gdn.gdn_ctx_status(ctx)
+    o_ref = oracle.verify_inputs(inp)
+    assert_close(o.cpu().numpy(), o_ref, "edge-of-stable o")
+    o_static = gdn.gdn_tree_verify_static(d["q"], d["k"], d["v"], d["g"], d["beta"], d["parent"], d["S0"])
+    torch.cuda.synchronize()
+    assert_close(o_static.cpu().numpy(), o_ref, "edge-of-stable o (allocation-free)")
+    acc = np.array([depth - 1, N - 1], np.int32)
+    S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
+    assert_close(S_new.cpu().numpy(), oracle.commit_inputs(inp, accepted=acc), "edge-of-stable S_new")
+    if N <= 128:
+        _, inp2 = _edge_of_stable_inputs(N, depth, seed=32)
+        d2 = G.to_device(inp2)
+        o2, S2 = gdn.gdn_commit_verify(ctx, torch.from_numpy(acc).cuda(), d2["q"], d2["k"], d2["v"], d2["g"],
+                                       d2["beta"], d2["parent"])
+        torch.cuda.synchronize()
+        S_ref = oracle.commit_inputs(inp, accepted=acc)
+        assert_close(S2.cpu().numpy(), S_ref, "edge-of-stable fused S_next")
+        assert_close(o2.cpu().numpy(), oracle.verify_inputs(dict(inp2, S0=S_ref)), "edge-of-stable fused o")
+
+
 def test_side_stream():
     """verify and commit launched on a stream other than the current one
     (default priority), ordered only by that stream"""
