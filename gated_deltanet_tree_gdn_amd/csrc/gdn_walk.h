@@ -139,13 +139,9 @@ __device__ void walk_verify_slice_lds(const VerifyArgs& a, int b, int h, int c0,
     const T* __restrict__ v = static_cast<const T*>(a.v);
 
     const float* S0row = a.S0 + ((static_cast<size_t>(b) * Hv + h) * DV + c) * DK;
-    const float* s0p = S0row;
-    int s0_step = 1;
     if (s0_s) {
         for (int j = 0; j < DK; ++j) s0_s[j * 64 + lane] = S0row[j];
         Sync::sync();
-        s0p = s0_s + lane;
-        s0_step = 64;
     }
 
     for (int i = 0; i < N; ++i) {
@@ -161,11 +157,21 @@ __device__ void walk_verify_slice_lds(const VerifyArgs& a, int b, int h, int c0,
         Sync::sync();
         if (lane == 0) G_s[i] = Gi;
 
+        // two loops, so that each source keeps its address space (one
+        // pointer that may be either would take generic loads)
         float sk = 0.f, sq = 0.f;
-        for (int j = 0; j < DK; ++j) {
-            const float sv = s0p[j * s0_step];
-            sk += sv * ki_s[j];
-            sq += sv * qi_s[j];
+        if (s0_s) {
+            for (int j = 0; j < DK; ++j) {
+                const float sv = s0_s[j * 64 + lane];
+                sk += sv * ki_s[j];
+                sq += sv * qi_s[j];
+            }
+        } else {
+            for (int j = 0; j < DK; ++j) {
+                const float sv = S0row[j];
+                sk += sv * ki_s[j];
+                sq += sv * qi_s[j];
+            }
         }
         float self_qk = 0.f;
         for (int j = lane; j < DK; j += 64) self_qk += qi_s[j] * ki_s[j];

@@ -596,6 +596,28 @@ def test_solve_at_edge_of_stable_range(N, depth):
         assert_close(o2.cpu().numpy(), oracle.verify_inputs(dict(inp2, S0=S_ref)), "edge-of-stable fused o")
 
 
+def test_tree_runs_span_sequences():
+    """the two-launch verify's tree kernel walks runs of consecutive
+    (sequence, key head) items, one run per compute unit: with B H_k = 300
+    items on 256 compute units a run is two items and every other run
+    starts in one sequence and ends in the next; sequence 37 is a chain
+    deeper than 24 nodes (walked per node by the dense kernel) between
+    ordinary trees"""
+    cfg = G.shrink(G.CONFIGS["bestfirst128"], B=100, H_k=3, H_v=6, N=140, max_depth=24, d_k=64, d_v=64)
+    inp = G.make_inputs(cfg, seed=41)
+    par = inp["parent"].copy()
+    par[37] = np.arange(-1, cfg.N - 1, dtype=np.int32)
+    inp["parent"] = par
+    d = G.to_device(inp)
+    say("[runs span sequences] B=100 H_k=3 N=140")
+    o, ctx = run_verify(d)
+    gdn.gdn_ctx_status(ctx)
+    assert_close(o.cpu().numpy(), oracle.verify_inputs(inp), "runs span sequences o")
+    acc = np.random.default_rng(41).integers(-1, cfg.N, size=cfg.B).astype(np.int32)
+    S_new = gdn.gdn_commit_path(ctx, torch.from_numpy(acc).cuda())
+    assert_close(S_new.cpu().numpy(), oracle.commit_inputs(inp, accepted=acc), "runs span sequences S_new")
+
+
 def test_side_stream():
     """verify and commit launched on a stream other than the current one
     (default priority), ordered only by that stream"""
