@@ -363,6 +363,7 @@ def test_relabelled_tree_permutes_outputs():
     dict(N=33, tree="uniform"), dict(dtype="f32", N=70),
     dict(N=64, tree="chain"), dict(N=128, tree="chain"), dict(N=200, tree="uniform"),
     dict(N=160, d_k=64, d_v=128), dict(N=256, d_k=128, d_v=64, max_depth=24), dict(N=140, d_k=64, d_v=64),
+    dict(N=180, H_k=2, H_v=6, max_depth=24), dict(N=150, H_k=4, H_v=4, max_depth=24),
 ])
 def test_edge_shapes(shape):
     base = G.shrink(G.CONFIGS["bestfirst128"], B=2, H_k=2, H_v=4)
