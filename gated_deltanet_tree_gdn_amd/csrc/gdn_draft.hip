@@ -85,28 +85,31 @@ __global__ __launch_bounds__(64) void accept_kernel(int N, const int32_t* __rest
 // within a position the list order is the rank order), after which that
 // position's head moves on.  A step pops up to w heads; the nodes it places
 // get their own heads only when the step ends.
-// Wave-wide max / min with DPP row operations (pairs, quads, half rows,
-// rows, then the row broadcasts 15 and 31); the result is read from lane 63
-// and returned to every lane.
-template <typename T, typename Op>
-__device__ __forceinline__ T wave_reduce(T v, Op op) {
-    int x = static_cast<int>(v);
-    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false))));
-    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false))));
-    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false))));
-    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false))));
-    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false))));
-    x = static_cast<int>(op(static_cast<T>(x), static_cast<T>(__builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false))));
-    return static_cast<T>(__builtin_amdgcn_readlane(x, 63));
+
+// Wave-wide max of a 64-bit key with DPP row operations (pairs, quads, half
+// rows, rows, then the row broadcasts 15 and 31), both halves moved
+// together; the result is read from lane 63 and returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    int lo = static_cast<int>(static_cast<uint32_t>(v)), hi = static_cast<int>(static_cast<uint32_t>(v >> 32));
+    auto stage = [&](int lo2, int hi2) {
+        const uint64_t a = (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+        const uint64_t c = (static_cast<uint64_t>(static_cast<uint32_t>(hi2)) << 32) | static_cast<uint32_t>(lo2);
+        if (c > a) {
+            lo = lo2;
+            hi = hi2;
+        }
+    };
+    stage(__builtin_amdgcn_update_dpp(lo, lo, 0xB1, 0xF, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0xB1, 0xF, 0xF, false));
+    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x4E, 0xF, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x4E, 0xF, 0xF, false));
+    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x141, 0xF, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x141, 0xF, 0xF, false));
+    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x140, 0xF, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x140, 0xF, 0xF, false));
+    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x142, 0xA, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x142, 0xA, 0xF, false));
+    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x143, 0xC, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x143, 0xC, 0xF, false));
+    return (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, 63))) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, 63));
 }
 
-struct MaxU {
-    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; }
-};
-struct MinI {
-    __device__ int operator()(int a, int b) const { return a < b ? a : b; }
-};
-
+// An fp32 value as an unsigned integer of the same order.
 __device__ __forceinline__ uint32_t orderable(float x) {
     const uint32_t u = __float_as_uint(x);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -124,49 +127,70 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
     const int b = blockIdx.x, l = threadIdx.x;
     const float* rl = root_logp + static_cast<size_t>(b) * C;
     const float* nl = node_logp + static_cast<size_t>(b) * N * C;
-    bool unsorted = false;
-    for (int e = l; e < (N + 1) * C; e += 64) {
-        const int u = e / C, r = e % C;
-        const float x = u == 0 ? rl[r] : nl[static_cast<size_t>(u - 1) * C + r];
-        lp[u * kMaxCand + r] = x;
-        if (r > 0) {
-            const float prev = u == 0 ? rl[r - 1] : nl[static_cast<size_t>(u - 1) * C + r - 1];
-            unsorted |= x > prev;
+    // the candidate rows into LDS, eight loads in flight per lane at a time
+    // (entry e = u C + r: the prefix's row, then the nodes' rows, contiguous)
+    const int n_lp = (N + 1) * C;
+    for (int e0 = 0; e0 < n_lp; e0 += 64 * 8) {
+        float x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int e = min(e0 + l + 64 * q, n_lp - 1);
+            x[q] = e < C ? rl[e] : nl[static_cast<size_t>(e - C)];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int e = e0 + l + 64 * q;
+            if (e < n_lp) lp[(e / C) * kMaxCand + e % C] = x[q];
         }
     }
     if (l == 0) depth_s[0] = 0;
     __syncthreads();
+    // every row must be sorted best first
+    bool unsorted = false;
+    for (int e = l; e < n_lp; e += 64) {
+        const int u = e / C, r = e % C;
+        if (r > 0) unsorted |= lp[u * kMaxCand + r] > lp[u * kMaxCand + r - 1];
+    }
     const float NEG = -__builtin_inff();
     // head state per position held by this lane (u = l + 64 e)
     float hs[kU], ns[kU];   // head score; the position's own score
+    float nx[kU];           // log-probability of the candidate after the head
     int hr[kU];             // head rank
+    // the head as one key: the score's order in the high word, the
+    // position's in the low word (ties go to the lower position); 0: none
+    uint64_t hk[kU];
+    auto key_of = [](float score, int u) -> uint64_t {
+        return score == -__builtin_inff() ? 0ull
+                                          : (static_cast<uint64_t>(orderable(score)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(u));
+    };
 #pragma unroll
     for (int e = 0; e < kU; ++e) {
         hs[e] = NEG;
         ns[e] = 0.f;
+        nx[e] = NEG;
         hr[e] = 0;
+        hk[e] = 0ull;
     }
-    if (l == 0 && max_depth >= 1) hs[0] = lp[0];   // the prefix's best candidate
+    if (l == 0 && max_depth >= 1) {
+        hs[0] = lp[0];   // the prefix's best candidate
+        nx[0] = lp[min(1, C - 1)];
+        hk[0] = key_of(hs[0], 0);
+    }
     int count = 0, steps = 0;
     bool dry = false;
     while (count < N) {
         const int first = count;
         int taken = 0;
         while (taken < w && count < N) {
-            // this lane's best head, then the wavefront's
-            uint32_t key = 0u;
+            // this lane's best head, then the wavefront's: the best score,
+            // the lowest position among equals
+            uint64_t key = hk[0];
 #pragma unroll
-            for (int e = 0; e < kU; ++e) key = max(key, hs[e] == NEG ? 0u : orderable(hs[e]));
-            key = wave_reduce<uint32_t>(key, MaxU{});
-            if (key == 0u) break;   // every list is spent
-            // lowest position among the lanes holding that key (a lane's own
-            // best position is its lowest one with that key)
-            int cand = 0x7fffffff;
-#pragma unroll
-            for (int e = 0; e < kU; ++e)
-                if (hs[e] != NEG && orderable(hs[e]) == key) cand = min(cand, l + 64 * e);
-            cand = wave_reduce<int>(cand, MinI{});
-            const int u = cand, owner = u & 63, eo = u >> 6;
+            for (int e = 1; e < kU; ++e) key = hk[e] > key ? hk[e] : key;
+            key = wave_max_u64(key);
+            if (key == 0ull) break;   // every list is spent
+            const int u = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+            const int owner = u & 63, eo = u >> 6;
             if (l == owner) {
 #pragma unroll
                 for (int e = 0; e < kU; ++e)
@@ -176,9 +200,13 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
                         o_score[count] = hs[e];
                         const int nr = hr[e] + 1;
                         hr[e] = nr;
-                        // the prefix's candidates score their own log-probability
-                        const float x = lp[u * kMaxCand + min(nr, C - 1)];
+                        // the prefix's candidates score their own
+                        // log-probability; the one after the new head is read
+                        // now, for this position's next pop
+                        const float x = nx[e];
                         hs[e] = nr < C ? (u == 0 ? x : ns[e] + x) : NEG;
+                        hk[e] = key_of(hs[e], u);
+                        nx[e] = lp[u * kMaxCand + min(nr + 1, C - 1)];
                     }
             }
             ++count;
@@ -202,6 +230,8 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
                 ns[e] = o_score[j];
                 hr[e] = 0;
                 hs[e] = d < max_depth ? o_score[j] + lp[(j + 1) * kMaxCand] : NEG;
+                hk[e] = key_of(hs[e], j + 1);
+                nx[e] = lp[(j + 1) * kMaxCand + min(1, C - 1)];
             }
         }
         __syncthreads();
