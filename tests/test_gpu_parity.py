@@ -464,6 +464,7 @@ def _mixed_depth_inputs(cfg, seed, chain_every):
     dict(B=40, N=128, H_k=3, H_v=9),      # 2 heads per workgroup, sequence and key-head changes inside one
     dict(B=24, N=64, H_k=4, H_v=16),      # N <= 64 layout, 2 heads per workgroup
     dict(B=33, N=100, H_k=16, H_v=32),    # 5 heads per workgroup, ragged last workgroup
+    dict(B=128, N=128, H_k=16, H_v=32),   # 16 heads per workgroup: the hand-over slots cycle eight times
     dict(B=40, N=77, H_k=3, H_v=9, d_k=64, d_v=64),
     dict(B=40, N=128, H_k=9, H_v=9, d_k=64, d_v=128),
     dict(B=40, N=50, H_k=1, H_v=9, d_k=128, d_v=64),
