@@ -96,7 +96,11 @@ struct TreeLds {
     static constexpr int GG = BET + 8 * NMAX;            // float[2][NMAX]: G
     static constexpr int TMASK = GG + 8 * NMAX;          // uint32[NMAX / 16]: tile (I, J) holds pairs
     static constexpr int MISC = TMASK + 4 * (NMAX / 16); // int[16]
-    static constexpr int TOTAL = MISC + 64;
+    // uint32[NMAX / 32][NMAX]: word w of node i's ancestor set (i itself
+    // included), bit b for node 32 w + b; the words of consecutive nodes are
+    // consecutive, so four rows of one word are one 16-byte read
+    static constexpr int ANC = sp_align(MISC + 64, 16);
+    static constexpr int TOTAL = ANC + 4 * NMAX * (NMAX / 32);
 };
 
 // A persistent grid: one workgroup per compute unit, 2 NMAX threads, walking
@@ -165,6 +169,7 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w,
     float* Gs = reinterpret_cast<float*>(smem + L::GG);
     uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + L::TMASK);
     int* misc = reinterpret_cast<int*>(smem + L::MISC);
+    uint32_t* anc = reinterpret_cast<uint32_t*>(smem + L::ANC);
 
     // g and beta of value head kh R + r0 + hr at node ni
     auto load_gb = [&](int b, int kh, int r0, float& gi, float& bi) {
@@ -307,27 +312,38 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w,
             const uint4 v = row < N ? kv[q] : make_uint4(0u, 0u, 0u, 0u);
             *reinterpret_cast<uint4*>(Ks + row * L::KROW + cc * 16) = v;
         }
-        if (new_b && tid < NMAX && tid < N) {
-            // node i's root path, root first, at its pairs; the tiles that
-            // hold pairs; (key head 0) where each pair's entry goes in the
-            // dense kernel's blocks: block s / 32 (2 KB: 1 KB hi, then 1 KB
-            // lo) of the row tile, lane group (s / 4) mod 4, row i mod 16,
-            // slot 4 ((s / 16) mod 2) + s mod 4 of that lane's 8 bf16.  Key
-            // head 0 is always the first item of its sequence in a run.
+        if (new_b && tid < NMAX) {
+            // node i's root path, root first, at its pairs; its ancestor
+            // words; the tiles that hold pairs; (key head 0) where each
+            // pair's entry goes in the dense kernel's blocks: block s / 32
+            // (2 KB: 1 KB hi, then 1 KB lo) of the row tile, lane group
+            // (s / 4) mod 4, row i mod 16, slot 4 ((s / 16) mod 2) + s mod 4
+            // of that lane's 8 bf16.  Key head 0 is always the first item of
+            // its sequence in a run.
             const int i = tid;
-            uint16_t* zg = w.zoff + static_cast<size_t>(b) * w.P;
-            int pos = off[i] + dep[i] - 1;
-            uint32_t mask = 0u;
-            for (int s = i; s >= 0; s = par[s]) {
-                pathc[pos] = static_cast<uint8_t>(s);
-                if (kh == 0) {
-                    const int el = (((((s >> 2) & 3) << 4) | (i & 15)) << 3) + (((s >> 4) & 1) << 2) + (s & 3);
-                    zg[pos] = static_cast<uint16_t>(2048 * (s >> 5) + 2 * el);
+            constexpr int AW = NMAX / 32;
+            uint32_t am[AW];
+#pragma unroll
+            for (int q = 0; q < AW; ++q) am[q] = 0u;
+            if (i < N) {
+                uint16_t* zg = w.zoff + static_cast<size_t>(b) * w.P;
+                int pos = off[i] + dep[i] - 1;
+                uint32_t mask = 0u;
+                for (int s = i; s >= 0; s = par[s]) {
+                    pathc[pos] = static_cast<uint8_t>(s);
+                    if (kh == 0) {
+                        const int el = (((((s >> 2) & 3) << 4) | (i & 15)) << 3) + (((s >> 4) & 1) << 2) + (s & 3);
+                        zg[pos] = static_cast<uint16_t>(2048 * (s >> 5) + 2 * el);
+                    }
+                    --pos;
+                    mask |= 1u << (s >> 4);
+#pragma unroll
+                    for (int q = 0; q < AW; ++q) am[q] |= (s >> 5) == q ? 1u << (s & 31) : 0u;
                 }
-                --pos;
-                mask |= 1u << (s >> 4);
+                atomicOr(&tmask[i >> 4], mask);
             }
-            atomicOr(&tmask[i >> 4], mask);
+#pragma unroll
+            for (int q = 0; q < AW; ++q) anc[q * NMAX + i] = am[q];
         }
         __syncthreads();
         GDN_SPLIT_PHASE(3);
@@ -353,31 +369,27 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w,
                 bf16x8 ka[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) ka[ks] = k_frag(16 * I + lc, ks);
-                // this lane's rows i = 16 I + 4 lg + rr: first pair and depth
-                int oi[4], di[4];
+                // this lane's rows i = 16 I + 4 lg + rr: first pair
+                int oi[4];
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int i = 16 * I + 4 * lg + rr;
-                    oi[rr] = off[i];
-                    di[rr] = i < N ? dep[i] : 0;
-                }
+                for (int rr = 0; rr < 4; ++rr) oi[rr] = off[16 * I + 4 * lg + rr];
                 // tiles J <= I that hold pairs, in order; the K fragments of
                 // tile J, the depth of its node s = 16 J + lc and the
-                // root-path bytes at which the lane's four pairs (i, s) would
-                // sit are read one tile ahead
+                // ancestor words of the lane's four rows that hold s's bit
+                // are read one tile ahead (none of these reads waits for
+                // another)
                 const uint32_t todo = tm & ((2u << I) - 1u);
                 struct Ahead {
                     bf16x8 kb[KS];
                     int ds;
-                    int pc[4];
+                    uint4 am;
                 };
                 auto read_ahead = [&](int J) __attribute__((always_inline)) {
                     Ahead r;
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) r.kb[ks] = k_frag(16 * J + lc, ks);
                     r.ds = dep[16 * J + lc];
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) r.pc[rr] = pathc[min(max(oi[rr] + r.ds - 1, 0), L::CAP - 1)];
+                    r.am = *reinterpret_cast<const uint4*>(anc + (J >> 1) * NMAX + 16 * I + 4 * lg);
                     return r;
                 };
                 uint32_t left = todo;
@@ -397,17 +409,16 @@ __global__ __launch_bounds__(2 * NMAX) void tree_kernel(VerifyArgs a, SplitWs w,
                     Ahead nx;
                     if (Jn >= 0) nx = read_ahead(Jn);
                     // lane: rows i = 16 I + 4 lg + rr, column node s = 16 J +
-                    // lc; s is an ancestor of i (or i) exactly when i's root
-                    // path holds s at position dep[s] - 1, where the pair is
-                    // stored
-                    const int sn = 16 * J + lc;
+                    // lc; when s is an ancestor of i (or i), the pair sits at
+                    // position dep[s] - 1 of i's root path; every other entry
+                    // goes to the spare slot CAP (no branches)
+                    const int sb = (16 * J + lc) & 31;
+                    const uint32_t amw[4] = {cur.am.x, cur.am.y, cur.am.z, cur.am.w};
 #pragma unroll
                     for (int rr = 0; rr < 4; ++rr) {
-                        if (cur.ds >= 1 && cur.ds <= di[rr] && cur.pc[rr] == sn) {
-                            const int pp = oi[rr] + cur.ds - 1;
-                            kk[pp] = akk[rr];
-                            qk[pp] = aqk[rr];
-                        }
+                        const int pp = (amw[rr] >> sb) & 1u ? oi[rr] + cur.ds - 1 : L::CAP;
+                        kk[pp] = akk[rr];
+                        qk[pp] = aqk[rr];
                     }
                     if (Jn < 0) break;
                     J = Jn;
