@@ -86,27 +86,31 @@ __global__ __launch_bounds__(64) void accept_kernel(int N, const int32_t* __rest
 // position's head moves on.  A step pops up to w heads; the nodes it places
 // get their own heads only when the step ends.
 
-// Wave-wide max of a 64-bit key with DPP row operations (pairs, quads, half
-// rows, rows, then the row broadcasts 15 and 31), both halves moved
-// together; the result is read from lane 63 and returned to every lane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    int lo = static_cast<int>(static_cast<uint32_t>(v)), hi = static_cast<int>(static_cast<uint32_t>(v >> 32));
-    auto stage = [&](int lo2, int hi2) {
-        const uint64_t a = (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
-        const uint64_t c = (static_cast<uint64_t>(static_cast<uint32_t>(hi2)) << 32) | static_cast<uint32_t>(lo2);
-        if (c > a) {
-            lo = lo2;
-            hi = hi2;
-        }
-    };
-    stage(__builtin_amdgcn_update_dpp(lo, lo, 0xB1, 0xF, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0xB1, 0xF, 0xF, false));
-    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x4E, 0xF, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x4E, 0xF, 0xF, false));
-    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x141, 0xF, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x141, 0xF, 0xF, false));
-    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x140, 0xF, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x140, 0xF, 0xF, false));
-    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x142, 0xA, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x142, 0xA, 0xF, false));
-    stage(__builtin_amdgcn_update_dpp(lo, lo, 0x143, 0xC, 0xF, false), __builtin_amdgcn_update_dpp(hi, hi, 0x143, 0xC, 0xF, false));
-    return (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(hi, 63))) << 32) |
-           static_cast<uint32_t>(__builtin_amdgcn_readlane(lo, 63));
+// The wavefront's largest 32-bit value, in every lane: DPP max stages over
+// pairs, quads, half rows, rows, then the row broadcasts 15 and 31, after
+// which lane 63 holds the maximum.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t max_stage_u32(uint32_t v) {
+    // lanes without a source read 0, the identity of the unsigned max
+    const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROW_MASK, 0xF, false));
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max_stage_u32<0xB1, 0xF>(v);
+    v = max_stage_u32<0x4E, 0xF>(v);
+    v = max_stage_u32<0x141, 0xF>(v);
+    v = max_stage_u32<0x140, 0xF>(v);
+    v = max_stage_u32<0x142, 0xA>(v);
+    v = max_stage_u32<0x143, 0xC>(v);
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+// The wavefront's largest 64-bit key as two 32-bit reductions: the largest
+// high word, then the largest low word among the lanes that hold it.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+    const uint32_t hi = wave_max_u32(static_cast<uint32_t>(v >> 32));
+    const uint32_t lo = wave_max_u32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 // An fp32 value as an unsigned integer of the same order.
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
             uint64_t key = hk[0];
 #pragma unroll
             for (int e = 1; e < kU; ++e) key = hk[e] > key ? hk[e] : key;
-            key = wave_max_u64(key);
+            key = wave_max_key(key);
             if (key == 0ull) break;   // every list is spent
             const int u = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
             const int owner = u & 63, eo = u >> 6;
