@@ -131,18 +131,19 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
     const int b = blockIdx.x, l = threadIdx.x;
     const float* rl = root_logp + static_cast<size_t>(b) * C;
     const float* nl = node_logp + static_cast<size_t>(b) * N * C;
-    // the candidate rows into LDS, eight loads in flight per lane at a time
+    // the candidate rows into LDS, 32 loads in flight per lane at a time
     // (entry e = u C + r: the prefix's row, then the nodes' rows, contiguous)
     const int n_lp = (N + 1) * C;
-    for (int e0 = 0; e0 < n_lp; e0 += 64 * 8) {
-        float x[8];
+    constexpr int LB = 32;
+    for (int e0 = 0; e0 < n_lp; e0 += 64 * LB) {
+        float x[LB];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < LB; ++q) {
             const int e = min(e0 + l + 64 * q, n_lp - 1);
             x[q] = e < C ? rl[e] : nl[static_cast<size_t>(e - C)];
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < LB; ++q) {
             const int e = e0 + l + 64 * q;
             if (e < n_lp) lp[(e / C) * kMaxCand + e % C] = x[q];
         }
