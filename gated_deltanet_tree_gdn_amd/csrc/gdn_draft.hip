@@ -150,11 +150,17 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
     }
     if (l == 0) depth_s[0] = 0;
     __syncthreads();
-    // every row must be sorted best first
+    // every row must be sorted best first (a lane walks whole rows)
     bool unsorted = false;
-    for (int e = l; e < n_lp; e += 64) {
-        const int u = e / C, r = e % C;
-        if (r > 0) unsorted |= lp[u * kMaxCand + r] > lp[u * kMaxCand + r - 1];
+    for (int u = l; u <= N; u += 64) {
+        const float* row = lp + u * kMaxCand;
+        float prev = row[0];
+#pragma unroll 8
+        for (int r = 1; r < C; ++r) {
+            const float x = row[r];
+            unsorted |= x > prev;
+            prev = x;
+        }
     }
     const float NEG = -__builtin_inff();
     // head state per position held by this lane (u = l + 64 e)
