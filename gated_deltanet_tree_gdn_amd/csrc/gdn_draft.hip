@@ -119,6 +119,8 @@ __device__ __forceinline__ uint32_t orderable(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// KU positions per lane (the prefix included): (N + 1 + 63) / 64, up to kU
+template <int KU>
 __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_depth,
                                                    const float* __restrict__ root_logp,
                                                    const float* __restrict__ node_logp, int32_t* parent,
@@ -164,18 +166,18 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
     }
     const float NEG = -__builtin_inff();
     // head state per position held by this lane (u = l + 64 e)
-    float hs[kU], ns[kU];   // head score; the position's own score
-    float nx[kU];           // log-probability of the candidate after the head
-    int hr[kU];             // head rank
+    float hs[KU], ns[KU];   // head score; the position's own score
+    float nx[KU];           // log-probability of the candidate after the head
+    int hr[KU];             // head rank
     // the head as one key: the score's order in the high word, the
     // position's in the low word (ties go to the lower position); 0: none
-    uint64_t hk[kU];
+    uint64_t hk[KU];
     auto key_of = [](float score, int u) -> uint64_t {
         return score == -__builtin_inff() ? 0ull
                                           : (static_cast<uint64_t>(orderable(score)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(u));
     };
 #pragma unroll
-    for (int e = 0; e < kU; ++e) {
+    for (int e = 0; e < KU; ++e) {
         hs[e] = NEG;
         ns[e] = 0.f;
         nx[e] = NEG;
@@ -197,14 +199,14 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
             // the lowest position among equals
             uint64_t key = hk[0];
 #pragma unroll
-            for (int e = 1; e < kU; ++e) key = hk[e] > key ? hk[e] : key;
+            for (int e = 1; e < KU; ++e) key = hk[e] > key ? hk[e] : key;
             key = wave_max_key(key);
             if (key == 0ull) break;   // every list is spent
             const int u = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
             const int owner = u & 63, eo = u >> 6;
             if (l == owner) {
 #pragma unroll
-                for (int e = 0; e < kU; ++e)
+                for (int e = 0; e < KU; ++e)
                     if (e == eo) {
                         o_par[count] = u - 1;
                         o_rank[count] = hr[e];
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(64) void build_kernel(int N, int C, int w, int max_
         // position's depth + 1, exchanged through LDS: the parent's depth
         // belongs to the lane that holds the parent)
 #pragma unroll
-        for (int e = 0; e < kU; ++e) {
+        for (int e = 0; e < KU; ++e) {
             const int j = l + 64 * e - 1;
             if (j >= first && j < count) {
                 const int d = depth_s[o_par[j] + 1] + 1;
@@ -273,8 +275,18 @@ hipError_t launch_accept(int B, int N, const int32_t* parent, const int32_t* dra
 hipError_t launch_build(int B, int N, int C, int w, int max_depth, const float* root_logp, const float* node_logp,
                         int32_t* parent, int32_t* cand_rank, float* score, int32_t* steps, int32_t* build_status,
                         hipStream_t stream) {
-    hipLaunchKernelGGL(build_kernel, dim3(B), dim3(64), 0, stream, N, C, w, max_depth, root_logp, node_logp, parent,
-                       cand_rank, score, steps, build_status);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(B), dim3(64), 0, stream, N, C, w, max_depth, root_logp, node_logp, parent,
+                           cand_rank, score, steps, build_status);
+    };
+    static_assert(kU == 5, "one instantiation per count of positions per lane");
+    switch ((N + 1 + 63) / 64) {
+        case 1: go(build_kernel<1>); break;
+        case 2: go(build_kernel<2>); break;
+        case 3: go(build_kernel<3>); break;
+        case 4: go(build_kernel<4>); break;
+        default: go(build_kernel<5>); break;
+    }
     return hipGetLastError();
 }
 

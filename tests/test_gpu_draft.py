@@ -125,7 +125,8 @@ def check_build(root, node, w, cap, what):
     say(f"  {what}: steps {int(want[3].max())}, max depth {G.tree_stats(want[0])['max_depth']}")
 
 
-@pytest.mark.parametrize("N,cap", [(128, 16), (256, 24), (64, 16)])
+# N = 64, 128, 200, 256: two to five positions per lane in the kernel
+@pytest.mark.parametrize("N,cap", [(128, 16), (256, 24), (64, 16), (200, 24)])
 @pytest.mark.parametrize("w", [1, 4, 16, 64])
 def test_build_matches_reference(N, cap, w):
     rng = G.rng_for(N + w, 510)
