@@ -135,6 +135,16 @@ def test_build_matches_reference(N, cap, w):
     check_build(root, node, w, cap, f"N={N} w={w}")
 
 
+@pytest.mark.parametrize("N", [63, 127, 191, 254])
+def test_build_full_lanes(N):
+    # the largest N for one to four positions per lane (the prefix is a
+    # position too): every lane's last head slot holds a position
+    rng = G.rng_for(N, 512)
+    root, node = G.make_candidate_logp(rng, 32, N, 8)
+    say(f"[build] B=32 N={N} w=4 cap=24")
+    check_build(root, node, 4, 24, f"N={N} w=4")
+
+
 def test_build_edge_cases():
     rng = G.rng_for(1, 511)
     say("[build] edge cases")
